@@ -1,0 +1,32 @@
+"""fp64 CPU oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, header,
+helper or constant with the HIP library under ``io_aware_transformer_amd/``
+and imports nothing from it.
+
+The oracle is the plain definition of attention (materialise the score
+matrix, stable row softmax, multiply by V) and the textbook analytic
+backward, in float64, one (batch, query-head) unit at a time.  Every
+function cites the passage of the source pages it follows; see
+``oracle/attention.py``.
+"""
+
+from .attention import (
+    attention_forward,
+    attention_backward,
+    attention_forward_rows,
+    head_forward,
+    head_backward,
+    kv_head_of,
+)
+
+__all__ = [
+    "attention_forward",
+    "attention_backward",
+    "attention_forward_rows",
+    "head_forward",
+    "head_backward",
+    "kv_head_of",
+]

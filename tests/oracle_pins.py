@@ -1,0 +1,342 @@
+"""Pins that tie the fp64 oracle to facts fixed by the pages and by mathematics.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees
+with the fact it pins.  ``test_oracle_pins.py`` runs them against the oracle
+as written; ``test_oracle_mutants.py`` runs them against deliberately broken
+copies of the oracle's internals (a dropped scale, a wrong mask, a missing
+term, a transposed operand ...) and requires each break to be caught.
+
+The checks look the oracle up through the ``oracle.attention`` module at call
+time, so a patched module attribute is what they exercise.
+"""
+
+import math
+import os
+
+import numpy as np
+
+import oracle.attention as OA
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_four_token_example():
+    """Parse tests/golden/four_token_scores.txt -> dict name -> int matrix."""
+    blocks, name = {}, None
+    with open(os.path.join(GOLDEN, "four_token_scores.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line[0].isalpha():
+                name = line
+                blocks[name] = []
+            else:
+                blocks[name].append([int(x) for x in line.split()])
+    return {k: np.array(v, dtype=np.float64) for k, v in blocks.items()}
+
+
+def online_recurrence(scores, values, block):
+    """The pages' block recurrence, written independently of the oracle.
+
+    Interview Q&A (app.wittybyte.ai, "FlashAttention1"), softmax answer: for
+    block i, m_i = max(m_{i-1}, local_max_i) and
+    l_i = l_{i-1} exp(m_{i-1} - m_i) + local_sum_i exp(local_max_i - m_i),
+    with local_sum_i read as sum exp(s - local_max_i) over the block.  The
+    deep-dive page ("Intuition") rescales the numerator (the running output)
+    by the same factor as the denominator.  Start: m = -inf, l = 0, o = 0; a
+    block whose entries are all -inf (masked) contributes nothing.
+    Returns (O rows, LSE) for a score matrix ``scores`` [n, n_k] and values
+    ``values`` [n_k, d].
+    """
+    n, nk = scores.shape
+    d = values.shape[1]
+    O = np.zeros((n, d))
+    LSE = np.zeros(n)
+    for i in range(n):
+        m, l, o = -math.inf, 0.0, np.zeros(d)
+        for j0 in range(0, nk, block):
+            s = scores[i, j0 : j0 + block]
+            local_max = s.max()
+            if local_max == -math.inf:
+                continue
+            e = np.exp(s - local_max)
+            local_sum = e.sum()
+            local_o = e @ values[j0 : j0 + block]
+            m_new = max(m, local_max)
+            a_old = math.exp(m - m_new) if m != -math.inf else 0.0
+            a_new = math.exp(local_max - m_new)
+            l = l * a_old + local_sum * a_new
+            o = o * a_old + local_o * a_new
+            m = m_new
+        O[i] = o / l
+        LSE[i] = m + math.log(l)
+    return O, LSE
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# softmax of a row that is a permutation of [1, 2, 3, 4]: e^(x-4) / sum,
+# sum = 1 + e^-1 + e^-2 + e^-3 = 1.5530018...; values rounded to 7 digits.
+SOFTMAX_1234 = {1.0: 0.0320586, 2.0: 0.0871443, 3.0: 0.2368828, 4.0: 0.6439143}
+LSE_1234 = 4.4401897  # 4 + ln(1.5530018)
+L_MERGED = 1.5530018  # tile (A,B) then tile (C,D): 1.3678794 e^-2 + 1.3678794
+L_TILE = 1.3678794  # 1 + e^-1 for a 2-wide tile holding {x, x-1}
+
+
+def check_four_token_tiles_consistent():
+    ex = load_four_token_example()
+    s = ex["scores"]
+    assert np.array_equal(ex["tile1"], s[0:2, 0:2])
+    assert np.array_equal(ex["tile2"], s[0:2, 2:4])
+    assert np.array_equal(ex["tile3"], s[2:4, 0:2])
+    assert np.array_equal(ex["tile4"], s[2:4, 2:4])
+
+
+def check_four_token_recurrence_values():
+    """Row A through the pages' recurrence with 2-wide tiles, by hand."""
+    s = load_four_token_example()["scores"]
+    row = s[0]
+    # tile 1: local max 2, local sum 1 + e^-1; tile 2: local max 4, same sum
+    t1 = np.exp(row[:2] - row[:2].max()).sum()
+    t2 = np.exp(row[2:] - row[2:].max()).sum()
+    assert abs(t1 - L_TILE) < 1e-7 and abs(t2 - L_TILE) < 1e-7
+    m = max(row[:2].max(), row[2:].max())
+    l = t1 * math.exp(row[:2].max() - m) + t2 * math.exp(row[2:].max() - m)
+    assert m == 4.0 and abs(l - L_MERGED) < 1e-7
+    assert abs(m + math.log(l) - LSE_1234) < 1e-7
+
+
+def check_four_token_oracle():
+    """Oracle on the printed scores: Q = scores, K = I, V = I, scale 1."""
+    s = load_four_token_example()["scores"]
+    eye = np.eye(4)
+    Q, K, V = s[None, None], eye[None, None], eye[None, None]
+    O, LSE = OA.attention_forward(Q, K, V, 1.0, False)
+    for i in range(4):
+        want = np.array([SOFTMAX_1234[x] for x in s[i]])
+        assert np.max(np.abs(O[0, 0, i] - want)) < 1e-7, (i, O[0, 0, i], want)
+        assert abs(LSE[0, 0, i] - LSE_1234) < 1e-7
+    # the same with every score shifted by 1000: weights unchanged, LSE + 1000
+    # (softmax is invariant to a per-row constant; the stable form must not
+    # overflow)
+    O2, LSE2 = OA.attention_forward((s + 1000.0)[None, None] * 1.0, K, V, 1.0, False)
+    assert np.all(np.isfinite(O2)) and np.all(np.isfinite(LSE2))
+    assert np.max(np.abs(O2 - O)) < 1e-12
+    assert np.max(np.abs(LSE2 - (LSE + 1000.0))) < 1e-9
+    # the pages' recurrence over the printed 2 x 2 tiling gives the same
+    O3, LSE3 = online_recurrence(s, eye, 2)
+    assert np.max(np.abs(O3 - O[0, 0])) < 1e-14
+    assert np.max(np.abs(LSE3 - LSE[0, 0])) < 1e-14
+
+
+def check_blocked_recurrence_matches(seed=7):
+    rng = np.random.default_rng(seed)
+    n, d, scale = 13, 5, 0.37
+    q, k, v = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    for causal in (False, True):
+        O, LSE = OA.attention_forward(q[None, None], k[None, None], v[None, None], scale, causal)
+        s = scale * (q @ k.T)
+        if causal:
+            s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+        for block in (1, 2, 3, 7, n):
+            Ob, LSEb = online_recurrence(s, v, block)
+            assert np.max(np.abs(Ob - O[0, 0])) < 1e-12, (causal, block)
+            assert np.max(np.abs(LSEb - LSE[0, 0])) < 1e-12, (causal, block)
+
+
+def check_rows_sum_to_one(seed=8):
+    rng = np.random.default_rng(seed)
+    n = 11
+    q, k = _rand(rng, n, 6), _rand(rng, n, 6)
+    eye = np.eye(n)
+    for causal in (False, True):
+        O, _ = OA.attention_forward(q[None, None], k[None, None], eye[None, None], 0.5, causal)
+        P = O[0, 0]
+        assert np.all(P >= 0)
+        assert np.max(np.abs(P.sum(axis=1) - 1.0)) < 1e-14
+        if causal:
+            assert np.all(P[np.triu_indices(n, 1)] == 0.0)
+
+
+def check_constant_v(seed=9):
+    rng = np.random.default_rng(seed)
+    n, d = 10, 4
+    q, k, do = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    c = rng.standard_normal(d)
+    v = np.tile(c, (n, 1))
+    for causal in (False, True):
+        O, _ = OA.attention_forward(q[None, None], k[None, None], v[None, None], 0.8, causal)
+        assert np.max(np.abs(O[0, 0] - c)) < 1e-14
+        dQ, dK, dV = OA.attention_backward(q[None, None], k[None, None], v[None, None], do[None, None], 0.8, causal)
+        assert np.max(np.abs(dQ)) < 1e-13 and np.max(np.abs(dK)) < 1e-13
+
+
+def check_equal_scores(seed=10):
+    rng = np.random.default_rng(seed)
+    n, d = 9, 3
+    k, v = _rand(rng, n, d), _rand(rng, n, d)
+    q = np.zeros((n, d))
+    O, LSE = OA.attention_forward(q[None, None], k[None, None], v[None, None], 1.3, False)
+    assert np.max(np.abs(O[0, 0] - v.mean(axis=0))) < 1e-14
+    assert np.max(np.abs(LSE[0, 0] - math.log(n))) < 1e-14
+    O, LSE = OA.attention_forward(q[None, None], k[None, None], v[None, None], 1.3, True)
+    prefix_mean = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.max(np.abs(O[0, 0] - prefix_mean)) < 1e-14
+    assert np.max(np.abs(LSE[0, 0] - np.log(np.arange(1, n + 1)))) < 1e-14
+    # scale = 0 makes every score equal as well
+    q2 = _rand(rng, n, d)
+    O, LSE = OA.attention_forward(q2[None, None], k[None, None], v[None, None], 0.0, True)
+    assert np.max(np.abs(O[0, 0] - prefix_mean)) < 1e-14
+
+
+def check_single_token(seed=11):
+    rng = np.random.default_rng(seed)
+    d, scale = 5, 0.6
+    q, k, v, do = (_rand(rng, 1, d) for _ in range(4))
+    for causal in (False, True):
+        O, LSE = OA.attention_forward(q[None, None], k[None, None], v[None, None], scale, causal)
+        assert np.array_equal(O[0, 0], v)
+        assert abs(LSE[0, 0, 0] - scale * float(q[0] @ k[0])) < 1e-15
+        dQ, dK, dV = OA.attention_backward(q[None, None], k[None, None], v[None, None], do[None, None], scale, causal)
+        assert np.max(np.abs(dQ)) < 1e-15 and np.max(np.abs(dK)) < 1e-15
+        assert np.max(np.abs(dV[0, 0] - do)) < 1e-15
+
+
+def check_causal_prefix(seed=12):
+    rng = np.random.default_rng(seed)
+    n, d, scale = 8, 4, 0.7
+    q, k, v = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    O, LSE = OA.attention_forward(q[None, None], k[None, None], v[None, None], scale, True)
+    for i in range(n):
+        Oi, LSEi = OA.attention_forward(
+            q[None, None, : i + 1], k[None, None, : i + 1], v[None, None, : i + 1], scale, False
+        )
+        assert np.max(np.abs(O[0, 0, i] - Oi[0, 0, i])) < 1e-14
+        assert abs(LSE[0, 0, i] - LSEi[0, 0, i]) < 1e-14
+    assert np.array_equal(O[0, 0, 0], v[0])
+
+
+def _loss(Q, K, V, dO, scale, causal):
+    O, _ = OA.attention_forward(Q, K, V, scale, causal)
+    return float((O * dO).sum())
+
+
+def check_backward_finite_differences(seed=13):
+    """Central differences of L = <dO, O> against the analytic backward."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, n, d, scale = 1, 2, 1, 6, 3, 0.45
+    Q = rng.standard_normal((B, Hq, n, d))
+    K = rng.standard_normal((B, Hkv, n, d))
+    V = rng.standard_normal((B, Hkv, n, d))
+    dO = rng.standard_normal((B, Hq, n, d))
+    h = 1e-6
+    for causal in (False, True):
+        grads = OA.attention_backward(Q, K, V, dO, scale, causal)
+        for which, X in enumerate((Q, K, V)):
+            G = grads[which]
+            num = np.zeros_like(X)
+            it = np.nditer(X, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                old = X[idx]
+                X[idx] = old + h
+                lp = _loss(Q, K, V, dO, scale, causal)
+                X[idx] = old - h
+                lm = _loss(Q, K, V, dO, scale, causal)
+                X[idx] = old
+                num[idx] = (lp - lm) / (2 * h)
+            err = np.max(np.abs(num - G)) / max(1.0, np.max(np.abs(G)))
+            assert err < 1e-7, (causal, which, err)
+
+
+def check_against_torch_sdpa(seed=14):
+    """Library cross-check: torch's CPU float64 scaled_dot_product_attention
+    (and its autograd) on the same inputs, including grouped heads."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, n, d, scale = 2, 4, 2, 7, 5, 0.31
+    Q = rng.standard_normal((B, Hq, n, d))
+    K = rng.standard_normal((B, Hkv, n, d))
+    V = rng.standard_normal((B, Hkv, n, d))
+    dO = rng.standard_normal((B, Hq, n, d))
+    for causal in (False, True):
+        O, LSE = OA.attention_forward(Q, K, V, scale, causal)
+        dQ, dK, dV = OA.attention_backward(Q, K, V, dO, scale, causal)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+        to = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale, enable_gqa=True)
+        to.backward(torch.tensor(dO))
+        assert np.max(np.abs(O - to.detach().numpy())) < 1e-12
+        assert np.max(np.abs(dQ - tq.grad.numpy())) < 1e-12
+        assert np.max(np.abs(dK - tk.grad.numpy())) < 1e-12
+        assert np.max(np.abs(dV - tv.grad.numpy())) < 1e-12
+        # LSE: torch.logsumexp over the scaled, masked scores of each head
+        kk = torch.tensor(K).repeat_interleave(Hq // Hkv, dim=1)
+        s = torch.tensor(Q) @ kk.transpose(-1, -2) * scale
+        if causal:
+            s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+        assert np.max(np.abs(LSE - torch.logsumexp(s, dim=-1).numpy())) < 1e-12
+
+
+def check_grouped_heads(seed=15):
+    """GQA equals MHA over K/V repeated per group; dK/dV are group sums."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, n, d, scale = 1, 6, 2, 5, 3, 0.5
+    G = Hq // Hkv
+    Q = rng.standard_normal((B, Hq, n, d))
+    K = rng.standard_normal((B, Hkv, n, d))
+    V = rng.standard_normal((B, Hkv, n, d))
+    dO = rng.standard_normal((B, Hq, n, d))
+    Kr, Vr = np.repeat(K, G, axis=1), np.repeat(V, G, axis=1)
+    for causal in (False, True):
+        O, LSE = OA.attention_forward(Q, K, V, scale, causal)
+        Or, LSEr = OA.attention_forward(Q, Kr, Vr, scale, causal)
+        assert np.max(np.abs(O - Or)) < 1e-14 and np.max(np.abs(LSE - LSEr)) < 1e-14
+        dQ, dK, dV = OA.attention_backward(Q, K, V, dO, scale, causal)
+        dQr, dKr, dVr = OA.attention_backward(Q, Kr, Vr, dO, scale, causal)
+        assert np.max(np.abs(dQ - dQr)) < 1e-14
+        assert np.max(np.abs(dK - dKr.reshape(B, Hkv, G, n, d).sum(axis=2))) < 1e-13
+        assert np.max(np.abs(dV - dVr.reshape(B, Hkv, G, n, d).sum(axis=2))) < 1e-13
+    assert [OA.kv_head_of(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+
+
+def check_forward_rows(seed=16):
+    """Row-sampled forward equals the full forward and the closed forms."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, n, d, scale = 2, 4, 2, 9, 4, 0.4
+    Q = rng.standard_normal((B, Hq, n, d))
+    K = rng.standard_normal((B, Hkv, n, d))
+    V = rng.standard_normal((B, Hkv, n, d))
+    for causal in (False, True):
+        O, LSE = OA.attention_forward(Q, K, V, scale, causal)
+        rows = [0, 3, n - 1]
+        Or, LSEr = OA.attention_forward_rows(Q, K, V, scale, causal, 1, 3, rows)
+        assert np.max(np.abs(Or - O[1, 3, rows])) < 1e-14
+        assert np.max(np.abs(LSEr - LSE[1, 3, rows])) < 1e-14
+    Z = np.zeros_like(Q)
+    Or, LSEr = OA.attention_forward_rows(Z, K, V, scale, True, 0, 2, [0, 4, 8])
+    g = OA.kv_head_of(2, Hq, Hkv)
+    for t, i in enumerate([0, 4, 8]):
+        assert np.max(np.abs(Or[t] - V[0, g, : i + 1].mean(axis=0))) < 1e-14
+        assert abs(LSEr[t] - math.log(i + 1)) < 1e-14
+
+
+ALL_CHECKS = [
+    check_four_token_tiles_consistent,
+    check_four_token_recurrence_values,
+    check_four_token_oracle,
+    check_blocked_recurrence_matches,
+    check_rows_sum_to_one,
+    check_constant_v,
+    check_equal_scores,
+    check_single_token,
+    check_causal_prefix,
+    check_backward_finite_differences,
+    check_against_torch_sdpa,
+    check_grouped_heads,
+    check_forward_rows,
+]

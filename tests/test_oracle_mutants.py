@@ -1,0 +1,154 @@
+"""Each plausible mistake planted in a copy of the oracle must fail a pin.
+
+The mistakes are planted on the CPU by patching ``oracle.attention`` for the
+duration of one test; the oracle on disk is never changed.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.attention as OA
+import oracle_pins
+
+
+def _scores_no_scale(q, k, scale, causal):
+    return OA_orig["_scores"](q, k, 1.0, causal)
+
+
+def _scores_scale_twice(q, k, scale, causal):
+    return OA_orig["_scores"](q, k, scale * scale, causal)
+
+
+def _mask(q, k, scale, hide):
+    s = scale * (q @ k.T)
+    i = np.arange(q.shape[0])[:, None]
+    j = np.arange(k.shape[0])[None, :]
+    return np.where(hide(i, j), -np.inf, s)
+
+
+def _scores_mask_diagonal(q, k, scale, causal):
+    return _mask(q, k, scale, lambda i, j: j >= i) if causal else scale * (q @ k.T)
+
+
+def _scores_mask_transposed(q, k, scale, causal):
+    return _mask(q, k, scale, lambda i, j: j < i) if causal else scale * (q @ k.T)
+
+
+def _softmax_no_shift(s):
+    e = np.exp(s)
+    l = e.sum(axis=1)
+    return e / l[:, None], np.zeros(s.shape[0]), l
+
+
+def _softmax_no_norm(s):
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    return e, m, e.sum(axis=1)
+
+
+def _fwd_lse_no_max(q, k, v, scale, causal):
+    p, m, l = OA._row_softmax(OA._scores(np.asarray(q, float), np.asarray(k, float), scale, causal))
+    return p @ v, np.log(l)
+
+
+def _fwd_pt_v(q, k, v, scale, causal):
+    p, m, l = OA._row_softmax(OA._scores(np.asarray(q, float), np.asarray(k, float), scale, causal))
+    return p.T @ v, m + np.log(l)
+
+
+def _bwd_factory(change):
+    def bwd(q, k, v, do, scale, causal):
+        q, k, v, do = (np.asarray(x, float) for x in (q, k, v, do))
+        p, _, _ = OA._row_softmax(OA._scores(q, k, scale, causal))
+        dv = p.T @ do
+        dp = do @ v.T
+        d_row = (p * dp).sum(axis=1)
+        ds = p * (dp - d_row[:, None])
+        dq = scale * (ds @ k)
+        dk = scale * (ds.T @ q)
+        if change == "dv_no_transpose":
+            dv = p @ do
+        elif change == "ds_no_rowterm":
+            ds = p * dp
+            dq, dk = scale * (ds @ k), scale * (ds.T @ q)
+        elif change == "dk_no_scale":
+            dk = ds.T @ q
+        elif change == "dq_transposed":
+            dq = scale * (ds.T @ k)
+        elif change == "dp_sign":
+            ds = p * (d_row[:, None] - dp)
+            dq, dk = scale * (ds @ k), scale * (ds.T @ q)
+        return dq, dk, dv
+
+    return bwd
+
+
+def _kv_head_interleaved(h_q, n_heads_q, n_heads_kv):
+    return h_q % n_heads_kv
+
+
+def _rows_off_by_one(Q, K, V, scale, causal, b, h, rows):
+    B, Hq, Hkv, N, d = OA._check_shapes(Q, K, V)
+    g = OA.kv_head_of(h, Hq, Hkv)
+    o = np.zeros((len(rows), d))
+    lse = np.zeros(len(rows))
+    for t, i in enumerate(rows):
+        s = scale * (K[b, g] @ Q[b, h, i])
+        if causal:
+            s = s[: max(i, 1)]
+        m = s.max()
+        e = np.exp(s - m)
+        o[t] = (e / e.sum()) @ V[b, g, : s.shape[0]]
+        lse[t] = m + np.log(e.sum())
+    return o, lse
+
+
+def _bwd_group_overwrite(Q, K, V, dO, scale, causal):
+    B, Hq, Hkv, N, d = OA._check_shapes(Q, K, V)
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = OA.kv_head_of(h, Hq, Hkv)
+            dQ[b, h], dK[b, g], dV[b, g] = OA.head_backward(Q[b, h], K[b, g], V[b, g], dO[b, h], scale, causal)
+    return dQ, dK, dV
+
+
+OA_orig = {name: getattr(OA, name) for name in dir(OA) if not name.startswith("__")}
+
+MUTANTS = {
+    "scale_dropped": ("_scores", _scores_no_scale),
+    "scale_twice": ("_scores", _scores_scale_twice),
+    "mask_hides_diagonal": ("_scores", _scores_mask_diagonal),
+    "mask_transposed": ("_scores", _scores_mask_transposed),
+    "softmax_without_max_shift": ("_row_softmax", _softmax_no_shift),
+    "softmax_not_normalised": ("_row_softmax", _softmax_no_norm),
+    "lse_without_max": ("head_forward", _fwd_lse_no_max),
+    "output_uses_p_transposed": ("head_forward", _fwd_pt_v),
+    "dv_not_transposed": ("head_backward", _bwd_factory("dv_no_transpose")),
+    "ds_missing_row_term": ("head_backward", _bwd_factory("ds_no_rowterm")),
+    "dk_missing_scale": ("head_backward", _bwd_factory("dk_no_scale")),
+    "dq_transposed": ("head_backward", _bwd_factory("dq_transposed")),
+    "ds_sign_flipped": ("head_backward", _bwd_factory("dp_sign")),
+    "kv_heads_interleaved": ("kv_head_of", _kv_head_interleaved),
+    "rows_causal_off_by_one": ("attention_forward_rows", _rows_off_by_one),
+    "group_grads_overwritten": ("attention_backward", _bwd_group_overwrite),
+}
+
+
+def _caught(check):
+    try:
+        with np.errstate(all="ignore"):
+            check()
+    except AssertionError:
+        return True
+    except (ValueError, FloatingPointError, ZeroDivisionError, IndexError):
+        return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(OA, attr, fn)
+    caught = [c.__name__ for c in oracle_pins.ALL_CHECKS if _caught(c)]
+    assert caught, f"no pin catches mutant {name}"
