@@ -1,0 +1,147 @@
+/*
+ * fa.h -- C ABI of an exact scaled-dot-product attention library for AMD
+ * MI355X (gfx950).  Forward and backward passes run as hand-written HIP
+ * kernels; this header has no HIP, C++ or framework types in it.
+ *
+ * What is computed (forward).  For every batch b and query head h, with
+ * key/value head g = h / (H_q / H_kv):
+ *
+ *     S  = scale * Q[b,h] K[b,g]^T            (N x N scores; with causal,
+ *                                              S[i][j] = -inf for j > i)
+ *     P  = row-softmax(S)
+ *     O[b,h]   = P V[b,g]
+ *     LSE[b,h][i] = ln sum_j exp(S[i][j])     (natural log)
+ *
+ * Sources: the standard attention walk-through (Steps 1-3) of the page
+ * "Flash attention: fast and memory-efficient exact attention with
+ * IO-awareness -- a deep dive"; the scale factor from "Optimizing memory
+ * usage on GPUs with flash attention mechanisms", section "Mechanics of Flash
+ * Attention"; grouped-query / multi-query head sharing and head dims up to
+ * 256 from "The Future of AI: How FlashAttention Revolutionizes Deep
+ * Learning", section "FlashAttention-2: Enhanced Performance".  The kernels
+ * evaluate it block by block with the running-max / running-sum recurrence
+ * given in the softmax answer of the FlashAttention interview Q&A
+ * (app.wittybyte.ai, "FlashAttention1"); the N x N matrices never reach
+ * device memory, and LSE is the per-row statistic kept for the backward
+ * pass (deep-dive page, "Intuition" under the softmax mathematics).
+ * The causal mask (j > i hidden, diagonal kept) and the natural-log LSE are
+ * readings: the pages do not define them.
+ *
+ * Memory layout.  All tensors are dense, row-major and contiguous:
+ *     Q, O, dO, dQ : [B][H_q ][N][d]
+ *     K, V, dK, dV : [B][H_kv][N][d]
+ *     LSE          : [B][H_q ][N]      always float32
+ * Elements of Q, K, V, O, dO, dQ, dK, dV are bfloat16 (FA_BF16) or float32
+ * (FA_FP32).  bfloat16 results are rounded to nearest even once, from
+ * float32 accumulators.
+ *
+ * Ownership and execution.  Every pointer argument is a DEVICE pointer owned
+ * by the caller; the library never allocates, frees or keeps a pointer after
+ * the call returns.  Work is enqueued on ``stream`` (a hipStream_t; NULL is
+ * the default stream) and the call returns without synchronising: outputs
+ * are valid once the stream reaches that point, and the caller keeps every
+ * buffer alive until then.  Outputs must not alias inputs.  Calls are
+ * thread-safe (the only shared state is a per-device property cache filled
+ * once).
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued;
+ * on an error nothing is launched and a negative FA_ERR_* code is returned.
+ * A failed HIP call returns FA_ERR_HIP; fa_last_hip_error() then gives the
+ * hipError_t value (thread-local).  fa_status_str() names a status code.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of Q, K, V, O, dO, dQ, dK, dV (LSE is always float32) */
+enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1 };
+
+/* status codes */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    FA_ERR_SHAPE = -2,       /* B, H_q, H_kv or N out of range, or H_q % H_kv   */
+    FA_ERR_HEADDIM = -3,     /* d not in {64, 128, 256}                         */
+    FA_ERR_DTYPE = -4,       /* dtype is not an fa_dtype value                  */
+    FA_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                */
+    FA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required         */
+    FA_ERR_UNSUPPORTED = -7, /* valid arguments, no kernel for this combination */
+    FA_ERR_HIP = -8,         /* a HIP runtime call failed (fa_last_hip_error)   */
+    FA_ERR_ARG = -9          /* causal not 0/1, or scale not finite             */
+};
+
+/* Largest sequence length and head count accepted (index arithmetic in the
+ * kernels is 64-bit for element offsets; these bound the grid). */
+#define FA_MAX_N (1 << 22)
+#define FA_MAX_HEADS 65535
+
+/*
+ * fa_fwd -- forward pass.
+ *   Q [B,H_q,N,d], K [B,H_kv,N,d], V [B,H_kv,N,d]   inputs (dtype)
+ *   O [B,H_q,N,d]                                    output (dtype)
+ *   LSE [B,H_q,N]                                    output (float32), may be
+ *                                                    NULL when not wanted
+ *   B >= 0, N >= 0 (B == 0 or N == 0: nothing to do, returns FA_OK and
+ *   pointers may be NULL), 1 <= H_kv <= H_q <= FA_MAX_HEADS, H_q % H_kv == 0,
+ *   N <= FA_MAX_N, d in {64, 128, 256}, causal in {0, 1}, scale finite.
+ *   N needs no relation to any tile size.  All pointers 16-byte aligned.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           int B, int H_q, int H_kv, int N, int d, float scale, int causal,
+           int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for these
+ * sizes (0 when there is nothing to do).  The workspace holds the per-row
+ * term D_i = sum_c dO[i][c] O[i][c] (float32 [B,H_q,N]).
+ */
+size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, int dtype);
+
+/*
+ * fa_bwd -- backward pass with on-chip recomputation of the scores.
+ *   Q, K, V                 the forward inputs
+ *   O, LSE                  the forward outputs of fa_fwd with the same
+ *                           scale, causal flag and dtype (LSE required here)
+ *   dO [B,H_q,N,d]          gradient of the loss with respect to O
+ *   dQ [B,H_q,N,d], dK, dV [B,H_kv,N,d]
+ *                           outputs, OVERWRITTEN (not accumulated into); for
+ *                           grouped heads dK/dV of a key/value head are the
+ *                           sums over the query heads of its group
+ *   workspace               device buffer of at least
+ *                           fa_bwd_workspace_size(...) bytes, 256-byte
+ *                           aligned; contents on entry are ignored
+ * The backward recomputes P from Q, K and LSE instead of storing it (page
+ * "The Future of AI ...", section "Understanding FlashAttention",
+ * recomputation).  The gradient formulas are the analytic derivative of the
+ * forward definition (the pages print none):
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij = dO_i . O_i,
+ *   dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ * Shapes and constraints as fa_fwd; d in {64, 128} for FA_BF16 (d = 256
+ * returns FA_ERR_UNSUPPORTED).
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
+           const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+           void* workspace, size_t workspace_bytes,
+           int B, int H_q, int H_kv, int N, int d, float scale, int causal,
+           int dtype, void* stream);
+
+/* Name of a status code ("FA_OK", "FA_ERR_SHAPE", ...); never NULL. */
+const char* fa_status_str(int status);
+
+/* hipError_t value behind the last FA_ERR_HIP returned on this thread
+ * (0 when none). */
+int fa_last_hip_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,12 @@
+"""Exact scaled-dot-product attention for AMD MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``include/fa.h`` (``libfa.so``); this package only marshals torch tensors
+into that ABI.  ``fwd``/``bwd`` raise ``LibraryNotBuilt`` when the library
+is missing -- there is no fallback path.
+"""
+
+from ._lib import FA_BF16, FA_FP32, FAError, LibraryNotBuilt, load as load_library
+from .attention import bwd, bwd_workspace_size, fwd
+
+__all__ = ["fwd", "bwd", "bwd_workspace_size", "FAError", "LibraryNotBuilt", "load_library", "FA_BF16", "FA_FP32"]

@@ -1,0 +1,91 @@
+"""ctypes loader for libfa.so and the C ABI declared in include/fa.h.
+
+Loading fails loudly (``LibraryNotBuilt``) when the library is missing:
+there is no fallback implementation of any entry point.
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+# enum fa_dtype
+FA_BF16 = 0
+FA_FP32 = 1
+
+# enum fa_status
+STATUS = {
+    0: "FA_OK",
+    -1: "FA_ERR_NULL",
+    -2: "FA_ERR_SHAPE",
+    -3: "FA_ERR_HEADDIM",
+    -4: "FA_ERR_DTYPE",
+    -5: "FA_ERR_ALIGN",
+    -6: "FA_ERR_WORKSPACE",
+    -7: "FA_ERR_UNSUPPORTED",
+    -8: "FA_ERR_HIP",
+    -9: "FA_ERR_ARG",
+}
+STATUS_CODE = {v: k for k, v in STATUS.items()}
+
+# every symbol include/fa.h declares
+EXPORTS = (
+    "fa_fwd",
+    "fa_bwd",
+    "fa_bwd_workspace_size",
+    "fa_status_str",
+    "fa_last_hip_error",
+    "fa_version",
+)
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class FAError(RuntimeError):
+    def __init__(self, status, where, hip_error=0):
+        self.status = status
+        self.hip_error = hip_error
+        name = STATUS.get(status, str(status))
+        extra = f" (hipError_t {hip_error})" if status == STATUS_CODE["FA_ERR_HIP"] else ""
+        super().__init__(f"{where} failed: {name}{extra}")
+
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+
+def load():
+    """Load libfa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryNotBuilt(
+            f"{LIB_PATH} is missing: build it with `python -m io_aware_transformer_amd.build`"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+    lib.fa_fwd.restype = _i
+    lib.fa_bwd.argtypes = [_vp] * 10 + [ctypes.c_size_t, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+    lib.fa_bwd.restype = _i
+    lib.fa_bwd_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_status_str.argtypes = [_i]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_last_hip_error.restype = _i
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = _i
+    _lib = lib
+    return lib
+
+
+def check(status, where):
+    if status != 0:
+        hip = load().fa_last_hip_error() if status == STATUS_CODE["FA_ERR_HIP"] else 0
+        raise FAError(status, where, hip)

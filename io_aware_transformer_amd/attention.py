@@ -1,0 +1,84 @@
+"""Torch-facing binding of the C ABI: argument marshalling only.
+
+``fwd`` and ``bwd`` check devices, dtypes, shapes and contiguity, allocate
+outputs with torch on the tensors' device, and pass raw device pointers plus
+the current HIP stream to ``fa_fwd`` / ``fa_bwd``.  Every step of the
+computation runs in the HIP kernels of libfa.so.
+"""
+
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.FA_BF16, torch.float32: _lib.FA_FP32}
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(q, k, v, *extra):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if not q.is_cuda:
+        raise ValueError("tensors must be on a HIP device")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t in (k, v, *extra):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on the same device")
+        if t.dtype != q.dtype:
+            raise TypeError("all tensors must share one dtype")
+    for t in (q, k, v, *extra):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k, v must be [B, H_kv, N, d] matching q")
+    return B, Hq, k.shape[1], N, d
+
+
+def fwd(q, k, v, scale=None, causal=True, out=None, lse=None):
+    """Forward pass: returns (o, lse).  o like q; lse float32 [B, H_q, N]."""
+    B, Hq, Hkv, N, d = _check(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    lib = _lib.load()
+    st = lib.fa_fwd(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        lse.data_ptr() or None, B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype],
+        _stream(q.device),
+    )
+    _lib.check(st, "fa_fwd")
+    return o, lse
+
+
+def bwd_workspace_size(B, Hq, Hkv, N, d, dtype=torch.bfloat16):
+    return int(_lib.load().fa_bwd_workspace_size(B, Hq, Hkv, N, d, _DTYPES[dtype]))
+
+
+def bwd(q, k, v, o, lse, do, scale=None, causal=True, workspace=None):
+    """Backward pass: returns (dq, dk, dv) shaped like q, k, v."""
+    B, Hq, Hkv, N, d = _check(q, k, v, o, do)
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H_q, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    lib = _lib.load()
+    st = lib.fa_bwd(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        do.data_ptr() or None, lse.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,
+        dv.data_ptr() or None, workspace.data_ptr() or None, workspace.numel(),
+        B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype], _stream(q.device),
+    )
+    _lib.check(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,130 @@
+// C ABI of the attention library: argument validation, kernel dispatch and
+// error reporting.  Every check runs on the host before any HIP call, so an
+// invalid call launches nothing and touches no device state.
+#include "fa.h"
+#include "fa_internal.h"
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_failure(hipError_t e) {
+    g_last_hip_error = int(e);
+    return FA_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape / scalar checks shared by fa_fwd and fa_bwd.
+int validate(int B, int Hq, int Hkv, int N, int d, float scale, int causal, int dtype) {
+    if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_DTYPE;
+    if (B < 0 || N < 0 || N > FA_MAX_N) return FA_ERR_SHAPE;
+    if (Hq < 1 || Hkv < 1 || Hq > FA_MAX_HEADS || Hkv > Hq || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_ARG;
+    // Grid bound: query blocks of 32 rows at the finest, times batch x heads.
+    const long long blocks = ((long long)N + 31) / 32 * (long long)B * (long long)Hq;
+    if (blocks > (long long)INT_MAX) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 100; }
+
+const char* fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULL: return "FA_ERR_NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE";
+        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM";
+        case FA_ERR_DTYPE: return "FA_ERR_DTYPE";
+        case FA_ERR_ALIGN: return "FA_ERR_ALIGN";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+        case FA_ERR_ARG: return "FA_ERR_ARG";
+        default: return "FA_ERR_UNKNOWN";
+    }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    if (B == 0 || N == 0) return FA_OK;
+    if (!Q || !K || !V || !O) return FA_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 16))
+        return FA_ERR_ALIGN;
+    fa::FwdParams p{};
+    p.Q = Q;
+    p.K = K;
+    p.V = V;
+    p.O = O;
+    p.LSE = LSE;
+    p.B = B;
+    p.Hq = H_q;
+    p.Hkv = H_kv;
+    p.N = N;
+    p.scale_log2 = scale * kLog2e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = (dtype == FA_BF16) ? fa::launch_fwd_bf16(p, d, causal, s) : fa::launch_fwd_f32(p, d, causal, s);
+    if (e != hipSuccess) return hip_failure(e);
+    return FA_OK;
+}
+
+size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, int dtype) {
+    if (validate(B, H_q, H_kv, N, d, 1.0f, 0, dtype) != FA_OK) return 0;
+    if (B == 0 || N == 0) return 0;
+    return fa::bwd_workspace_bytes(B, H_q, N);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+           void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    if (dtype == FA_BF16 && d == 256) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || N == 0) return FA_OK;
+    if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
+        !aligned(LSE, 16) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16))
+        return FA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < fa::bwd_workspace_bytes(B, H_q, N)) return FA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
+    fa::BwdParams p{};
+    p.Q = Q;
+    p.K = K;
+    p.V = V;
+    p.O = O;
+    p.dO = dO;
+    p.LSE = LSE;
+    p.dQ = dQ;
+    p.dK = dK;
+    p.dV = dV;
+    p.Drow = static_cast<float*>(workspace);
+    p.B = B;
+    p.Hq = H_q;
+    p.Hkv = H_kv;
+    p.N = N;
+    p.scale = scale;
+    p.scale_log2 = scale * kLog2e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = (dtype == FA_BF16) ? fa::launch_bwd_bf16(p, d, causal, s) : fa::launch_bwd_f32(p, d, causal, s);
+    if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
+    if (e != hipSuccess) return hip_failure(e);
+    return FA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Device-side building blocks for the gfx950 attention kernels.
+//
+// Matrix-core layouts (v_mfma_f32_32x32x16_bf16, one 64-lane wave; lane l,
+// half h = l / 32):
+//   A (32 x 16):  lane l holds A[l % 32][8h .. 8h+7]
+//   B (16 x 32):  lane l holds B[8h .. 8h+7][l % 32]
+//   C (32 x 32):  lane l, register r holds C[8(r/4) + 4h + r%4][l % 32]
+// LDS transpose read (ds_read_b64_tr_b16), per group of 16 lanes: lanes
+// 4e..4e+3 each address 4 consecutive 16-bit elements that together form
+// row e (16 elements); lane i of the group receives column i of rows 0..3.
+// v_permlane32_swap(x, x) returns {x[l % 32], x[32 + l % 32]} in every lane.
+// These were checked on the device with a layout probe before use.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte LDS / global vector access helpers.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Transposing 8-byte LDS read (see the layout note at the top).
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+#pragma clang diagnostic pop
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Max of x over lanes l and l^32 (the two halves of the wave).
+__device__ __forceinline__ float half_swap_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+// Sum of x over lanes l and l^32.
+__device__ __forceinline__ float half_swap_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+    return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round-to-nearest-even float -> bf16 pairs (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                            float a7) {
+    return bf16x8{(bf16)a0, (bf16)a1, (bf16)a2, (bf16)a3, (bf16)a4, (bf16)a5, (bf16)a6, (bf16)a7};
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile layouts.  A tile is `rows` x D bf16 stored as 16-byte chunks with
+// no padding; chunk c of row r lives at chunk slot r * (D/8) + swz(r, c).
+// The XOR swizzles keep the gfx950 LDS (64 banks x 4 bytes = 16 chunk slots
+// per bank row) free of conflicts for the access patterns that use them:
+//
+//  row-read layout (ds_read_b128 of one chunk from 16 consecutive rows):
+//    D >= 128: c ^ (r % 16)     D == 64: c ^ ((r / 2) % 8)
+//  transpose-read layout (ds_read_b64_tr_b16 of 4 chunks from 4 rows,
+//  rows r0..r0+3 with r0 % 4 == 0, chunks 4k..4k+3):
+//    D >= 128: c ^ 4(r % 4)     D == 64: c ^ 4((r / 2) % 2)
+// Writing whole rows (16 lanes = 16 consecutive chunks) is conflict-free in
+// both layouts.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz_row(int r, int c) {
+    if constexpr (D >= 128) return c ^ (r & 15);
+    else return c ^ ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_tr(int r, int c) {
+    if constexpr (D >= 128) return c ^ ((r & 3) << 2);
+    else return c ^ (((r >> 1) & 1) << 2);
+}
+// Element offset of (row r, element e) in a row-read tile.
+template <int D>
+__device__ __forceinline__ int off_row(int r, int e) {
+    return r * D + (swz_row<D>(r, e >> 3) << 3) + (e & 7);
+}
+template <int D>
+__device__ __forceinline__ int off_tr(int r, int e) {
+    return r * D + (swz_tr<D>(r, e >> 3) << 3) + (e & 7);
+}
+
+}  // namespace fa

@@ -1,0 +1,52 @@
+// Host-side interface between the C ABI (fa_api.cpp) and the kernel
+// launchers.  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+// Forward launch parameters.  Pointers are device pointers; element type is
+// bf16 or float depending on the launcher.  scale_log2 = scale * log2(e).
+struct FwdParams {
+    const void* Q;
+    const void* K;
+    const void* V;
+    void* O;
+    float* LSE;  // may be null
+    int B, Hq, Hkv, N;
+    float scale_log2;
+    int nqb;  // number of query blocks (filled by the launcher)
+};
+
+// Backward launch parameters.
+struct BwdParams {
+    const void* Q;
+    const void* K;
+    const void* V;
+    const void* O;
+    const void* dO;
+    const float* LSE;
+    void* dQ;
+    void* dK;
+    void* dV;
+    float* Drow;  // workspace: D_i = dO_i . O_i, float [B, Hq, N]
+    int B, Hq, Hkv, N;
+    float scale;       // softmax scale
+    float scale_log2;  // scale * log2(e)
+    int nqb, nkb;      // query / key blocks (filled by the launchers)
+};
+
+// Each launcher enqueues its kernels on `stream` and returns the first HIP
+// error (hipSuccess when everything was enqueued).  Shapes were validated
+// by the caller; d is one of the supported head dims for that launcher.
+hipError_t launch_fwd_bf16(FwdParams p, int d, int causal, hipStream_t stream);
+hipError_t launch_fwd_f32(FwdParams p, int d, int causal, hipStream_t stream);
+hipError_t launch_bwd_bf16(BwdParams p, int d, int causal, hipStream_t stream);
+hipError_t launch_bwd_f32(BwdParams p, int d, int causal, hipStream_t stream);
+
+// Workspace bytes of the backward for these sizes (D term only).
+size_t bwd_workspace_bytes(int B, int Hq, int N);
+
+}  // namespace fa

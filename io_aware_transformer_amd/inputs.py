@@ -1,0 +1,72 @@
+"""Seeded synthetic inputs: the only code shared by the HIP path's tests and
+the oracle's.  It draws random numbers and nothing else -- none of the
+attention arithmetic lives here.
+
+Recipe: a CPU ``torch.Generator`` seeded with the preset's seed draws
+standard-normal float32 tensors in the order Q, K, V, dO (each contiguous
+[B, H, N, d]; K and V use H_kv heads); bf16 presets round those values to
+bfloat16 (round to nearest even).  The same rounded values feed the GPU and,
+upcast exactly to float64, the oracle.
+"""
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Preset:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str  # "bf16" or "fp32"
+    causal: bool
+    seed: int
+    backward: bool = False
+
+    @property
+    def scale(self):
+        return self.d ** -0.5
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def describe(self):
+        return (f"{self.name}: B={self.B} H_q={self.Hq} H_kv={self.Hkv} N={self.N} d={self.d} "
+                f"{self.dtype} {'causal' if self.causal else 'non-causal'} seed={self.seed}")
+
+
+PRESETS = {
+    p.name: p
+    for p in [
+        Preset("c1", 1, 1, 1, 128, 64, "fp32", False, 101),
+        Preset("c2", 8, 16, 16, 2048, 128, "bf16", True, 201),
+        Preset("c3a", 2, 16, 16, 8192, 128, "bf16", True, 301),
+        Preset("c3b", 2, 32, 32, 8192, 64, "bf16", True, 302),
+        Preset("c4a", 4, 32, 8, 4096, 128, "bf16", True, 401),
+        Preset("c4b", 4, 32, 1, 4096, 128, "bf16", True, 402),
+        Preset("c4c", 4, 8, 8, 2048, 256, "bf16", True, 403),
+        Preset("c5", 4, 16, 16, 4096, 64, "bf16", True, 501, backward=True),
+    ]
+}
+
+
+def make(B, Hq, Hkv, N, d, dtype=torch.bfloat16, seed=0, with_grad=False):
+    """Q, K, V (and dO when ``with_grad``) as CPU tensors of ``dtype``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    out = [q, k, v]
+    if with_grad:
+        out.append(torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32))
+    return tuple(t.to(dtype) for t in out)
+
+
+def make_preset(p, with_grad=None):
+    return make(p.B, p.Hq, p.Hkv, p.N, p.d, p.torch_dtype, p.seed, p.backward if with_grad is None else with_grad)

@@ -1,0 +1,134 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/fa.h declares, and rejects invalid arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from io_aware_transformer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libfa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_functions():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_status_codes_match_binding():
+    text = open(HEADER).read()
+    for name, code in re.findall(r"(FA_(?:OK|ERR_[A-Z]+))\s*=\s*(-?\d+)", text):
+        assert _lib.STATUS[int(code)] == name
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    for code, name in _lib.STATUS.items():
+        assert lib.fa_status_str(code).decode() == name
+    assert lib.fa_status_str(12345).decode() == "FA_ERR_UNKNOWN"
+    assert lib.fa_version() == 100
+    assert lib.fa_last_hip_error() == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+MIS = 0x10008   # 8-byte aligned only
+
+
+def fwd(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125, causal=1,
+             dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_fwd(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                              a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+def bwd(ws_bytes=1 << 20, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, LSE=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE, ws=0x100000,
+             B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125, causal=1, dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_bwd(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"], a["dV"],
+                              a["ws"], ws_bytes, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"],
+                              a["causal"], a["dtype"], None)
+
+
+E = _lib.STATUS_CODE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), "FA_ERR_NULL"),
+    (dict(V=None), "FA_ERR_NULL"),
+    (dict(O=None), "FA_ERR_NULL"),
+    (dict(B=-1), "FA_ERR_SHAPE"),
+    (dict(N=-5), "FA_ERR_SHAPE"),
+    (dict(N=(1 << 22) + 1), "FA_ERR_SHAPE"),
+    (dict(Hq=0), "FA_ERR_SHAPE"),
+    (dict(Hkv=0), "FA_ERR_SHAPE"),
+    (dict(Hq=3, Hkv=2), "FA_ERR_SHAPE"),
+    (dict(Hq=2, Hkv=4), "FA_ERR_SHAPE"),
+    (dict(d=96), "FA_ERR_HEADDIM"),
+    (dict(d=0), "FA_ERR_HEADDIM"),
+    (dict(dtype=7), "FA_ERR_DTYPE"),
+    (dict(Q=MIS), "FA_ERR_ALIGN"),
+    (dict(LSE=MIS), "FA_ERR_ALIGN"),
+    (dict(causal=2), "FA_ERR_ARG"),
+    (dict(scale=float("nan")), "FA_ERR_ARG"),
+    (dict(scale=float("inf")), "FA_ERR_ARG"),
+])
+def test_fwd_rejects(kw, code):
+    assert fwd(**kw) == E[code]
+
+
+def test_fwd_empty_is_noop():
+    # nothing to compute: no pointer is touched, no kernel launched
+    assert fwd(Q=None, K=None, V=None, O=None, LSE=None, N=0) == 0
+    assert fwd(Q=None, K=None, V=None, O=None, LSE=None, B=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dO=None), "FA_ERR_NULL"),
+    (dict(LSE=None), "FA_ERR_NULL"),
+    (dict(dK=None), "FA_ERR_NULL"),
+    (dict(d=256), "FA_ERR_UNSUPPORTED"),
+    (dict(d=48), "FA_ERR_HEADDIM"),
+    (dict(dV=MIS), "FA_ERR_ALIGN"),
+    (dict(ws=0x100010), "FA_ERR_ALIGN"),
+    (dict(ws=None), "FA_ERR_WORKSPACE"),
+    (dict(Hq=4, Hkv=3), "FA_ERR_SHAPE"),
+])
+def test_bwd_rejects(kw, code):
+    assert bwd(**kw) == E[code]
+
+
+def test_bwd_workspace_too_small():
+    need = _lib.load().fa_bwd_workspace_size(1, 2, 1, 16, 64, _lib.FA_BF16)
+    assert need >= 2 * 16 * 4 and need % 256 == 0
+    assert bwd(ws_bytes=need - 1) == E["FA_ERR_WORKSPACE"]
+
+
+def test_workspace_size_formula():
+    lib = _lib.load()
+    # D term: float32 per (batch, query head, row), rounded up to 256 bytes
+    assert lib.fa_bwd_workspace_size(4, 16, 16, 4096, 64, _lib.FA_BF16) == 4 * 16 * 4096 * 4
+    assert lib.fa_bwd_workspace_size(1, 1, 1, 3, 64, _lib.FA_BF16) == 256
+    assert lib.fa_bwd_workspace_size(0, 1, 1, 3, 64, _lib.FA_BF16) == 0
+    assert lib.fa_bwd_workspace_size(1, 3, 2, 3, 64, _lib.FA_BF16) == 0  # invalid shape
+
+
+def test_bwd_empty_is_noop():
+    assert bwd(Q=None, K=None, V=None, O=None, dO=None, LSE=None, dQ=None, dK=None, dV=None, ws=None, N=0) == 0
