@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+A step is one forward pass (fa_fwd) followed by one backward pass (fa_bwd)
+of bf16 causal attention over one batch of seeded synthetic input that is
+already resident in device memory.  Default workload: B=8, H=16, N=2048,
+d=128 (the bf16 causal configuration the headline metric is quoted on).
+
+Throughput counts 4*B*H*N^2*d FLOP for the forward, halved for causal, and
+2.5x that for the backward.  Kernel time is taken with HIP events on the
+stream the kernels are launched on (torch's current stream).  Rank 0 prints
+one JSON line; see ``--help`` for the options.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 256 CUs x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(p, passes):
+    f = 4.0 * p.B * p.Hq * p.N * p.N * p.d
+    if p.causal:
+        f /= 2
+    total = 0.0
+    if "fwd" in passes:
+        total += f
+    if "bwd" in passes:
+        total += 2.5 * f
+    return total, f
+
+
+def alg_bytes_fwd(p):
+    """Algorithmic HBM bytes of one forward launch: Q, K, V read once, O
+    written once, LSE written (float32)."""
+    e = 2 if p.dtype == "bf16" else 4
+    return (2 * p.B * p.Hq * p.N * p.d + 2 * p.B * p.Hkv * p.N * p.d) * e + 4 * p.B * p.Hq * p.N
+
+
+def cpu_baseline(p, passes, budget_s):
+    """Time the fp64 oracle on host cores over (b, h) units of the same
+    workload until ``budget_s`` of CPU work is done (at least one unit)."""
+    import numpy as np
+
+    import oracle
+    from io_aware_transformer_amd import inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, k, v, do = inputs.make(1, 1, 1, p.N, p.d, p.torch_dtype, p.seed, with_grad=True)
+    q, k, v, do = (t[0, 0].float().numpy().astype(np.float64) for t in (q, k, v, do))
+    units = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.head_forward(q, k, v, p.scale, p.causal)
+        if "bwd" in passes:
+            oracle.head_backward(q, k, v, do, p.scale, p.causal)
+        units += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    unit_flops = flops(p, passes)[0] / (p.B * p.Hq)
+    return {
+        "value": round(units * unit_flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{units} (batch, head) units of N={p.N} d={p.d} ({'+'.join(passes)}) in {dt:.1f} s, "
+                  f"same FLOP count per unit as the GPU line",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--preset", default="c2", help="input preset (default c2: B8 H16 N2048 d128 bf16 causal)")
+    ap.add_argument("--passes", default="fwd,bwd", help="comma list of fwd,bwd")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline budget (0 disables)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU "
+              f"path; the per-GPU shard is the single-GPU workload.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from io_aware_transformer_amd import FAError, bwd, fwd, inputs
+
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    p = inputs.PRESETS[args.preset]
+    passes = [x for x in args.passes.split(",") if x]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    q, k, v, do = (t.to(dev) for t in inputs.make_preset(p, with_grad=True))
+    o, lse = fwd(q, k, v, scale=p.scale, causal=p.causal)
+    if "bwd" in passes:
+        try:
+            bwd(q, k, v, o, lse, do, scale=p.scale, causal=p.causal)
+        except FAError as e:
+            print(f"backward unavailable ({e}); timing the forward only", file=sys.stderr)
+            passes = [x for x in passes if x != "bwd"]
+    torch.cuda.synchronize()
+
+    ws = None
+    if "bwd" in passes:
+        from io_aware_transformer_amd import bwd_workspace_size
+
+        ws = torch.empty(max(1, bwd_workspace_size(p.B, p.Hq, p.Hkv, p.N, p.d, q.dtype)), device=dev,
+                         dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if "fwd" in passes:
+            fwd(q, k, v, scale=p.scale, causal=p.causal, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        if "bwd" in passes:
+            bwd(q, k, v, o, lse, do, scale=p.scale, causal=p.causal, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = total_ms / args.steps
+    total_flops, fwd_flops = flops(p, passes)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    def med(x):
+        x = sorted(x)
+        return x[len(x) // 2]
+
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    fwd_tflops = fwd_flops / (fwd_avg * 1e-3) / 1e12 if "fwd" in passes else None
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    bwd_tflops = 2.5 * fwd_flops / (bwd_avg * 1e-3) / 1e12 if "bwd" in passes else None
+
+    # Dominant kernel for the roofline: the forward kernel (one launch per
+    # fa_fwd call), bound by bf16 MFMA throughput.
+    roofline = {
+        "bound": "mfma",
+        "kernel": "fwd_bf16_kernel<%d,%s>" % (p.d, "true" if p.causal else "false"),
+        "achieved": round(fwd_tflops, 2) if fwd_tflops else None,
+        "peak": round(PEAK_BF16_TFLOPS, 1),
+        "unit": "TFLOP/s",
+        "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
+        "traffic": None,
+        "avg_launch_ms": round(fwd_avg, 5),
+        "alg_hbm_gbs": round(alg_bytes_fwd(p) / (fwd_avg * 1e-3) / 1e9, 1),
+    }
+    line = {
+        "metric": "attention fwd/bwd TFLOP/s (bf16, causal, d=128, N=2K-8K) + % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic: seeded N(0,1) Q, K, V, dO rounded to bf16, resident in HBM",
+        "config": {
+            "workload": f"{p.name}: {'+'.join(passes)} {p.dtype} {'causal' if p.causal else 'non-causal'} "
+                        f"attention B={p.B} H_q={p.Hq} H_kv={p.Hkv} N={p.N} d={p.d}",
+            "B": p.B, "H_q": p.Hq, "H_kv": p.Hkv, "N": p.N, "d": p.d, "causal": p.causal,
+            "passes": passes, "parallelism": "single GPU",
+        },
+        "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_tflops, 2) if fwd_tflops else None,
+        "fwd_ms_median": round(med(fwd_ms), 5),
+        "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
+        "bwd_ms_median": round(med(bwd_ms), 5) if "bwd" in passes else None,
+        "peak_inputs": {"cus": torch.cuda.get_device_properties(dev).multi_processor_count, "sclk_ghz": 2.4,
+                        "flop_per_clk_per_cu": 4096},
+        "roofline": roofline,
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(p, passes, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
