@@ -96,6 +96,23 @@ __device__ __forceinline__ int swz_tr(int r, int c) {
     if constexpr (D >= 128) return c ^ ((r & 3) << 2);
     else return c ^ (((r >> 1) & 1) << 2);
 }
+// Layout read both ways (row reads of 16 rows r0..r0+15 with r0 % 16 == 0,
+// and transpose reads of rows r0..r0+3 x chunks 4k..4k+3):
+//    D >= 128: c ^ (4(r % 4) | (r / 4) % 4)
+//    D == 64:  c ^ (4((r / 2) % 2) | (r / 4) % 4)
+// Row reads: the XOR term is a bijection over the 16 rows (per row parity
+// for D == 64), so one chunk column lands in 16 distinct slots.  Transpose
+// reads: the (r % 4) bits move whole 4-chunk groups, the (r / 4) bits
+// permute inside a group, giving 16 distinct slots for the 4 x 4 block.
+template <int D>
+__device__ __forceinline__ int swz_both(int r, int c) {
+    if constexpr (D >= 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    else return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int off_both(int r, int e) {
+    return r * D + (swz_both<D>(r, e >> 3) << 3) + (e & 7);
+}
 // Element offset of (row r, element e) in a row-read tile.
 template <int D>
 __device__ __forceinline__ int off_row(int r, int e) {

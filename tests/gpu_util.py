@@ -33,3 +33,48 @@ def maxabs(a, b):
     if a.size == 0:
         return 0.0
     return float(np.max(np.abs(a - b)))
+
+
+def bf16_half_ulp(x):
+    """Half the bf16 spacing at |x| (8 significant bits): the error that
+    rounding an exact result to bf16 can add by itself."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
+def check_half_ulp(got, want, slack, name=""):
+    """|got - want| <= half a bf16 ulp of want + slack, element by element
+    (for results that are exact before the final rounding to bf16)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(got - want)
+    bound = bf16_half_ulp(want) + slack
+    assert np.all(err <= bound), f"{name}: worst excess {np.max(err - bound)}"
+
+
+# Outside the fwd+bwd configurations (scale 1/sqrt(d), magnitudes below ~5)
+# the flat bound is scaled with the size of the exact result: bf16 operands
+# (P and dS rounded before the matrix products) and the bf16 O that enters
+# D_i = dO_i . O_i carry relative errors of order 2^-9, so for grouped heads
+# (dK/dV summing 4..32 heads) or sharper softmaxes (|scale| far above
+# 1/sqrt(d)) the absolute error grows with the magnitude of the gradients.
+REL_BF16 = 5e-3
+
+
+def check_close(got, want, base, rel=None, name=""):
+    """max |got - want| <= base, or <= max(base, rel * max|want|) when
+    ``rel`` is given.  Returns the max-abs error."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    err = np.abs(got - want)
+    top = float(np.max(np.abs(want)))
+    bound = base if rel is None else max(base, rel * top)
+    worst = float(err.max())
+    if worst > bound:
+        i = np.unravel_index(np.argmax(err), err.shape)
+        raise AssertionError(f"{name}: max-abs {worst} > bound {bound} at {i} (got {got[i]}, want {want[i]}, "
+                             f"max|want| {top})")
+    return worst
