@@ -90,6 +90,12 @@ def main():
     ap.add_argument("--preset", default="c2", help="input preset (default c2: B8 H16 N2048 d128 bf16 causal)")
     ap.add_argument("--passes", default="fwd,bwd", help="comma list of fwd,bwd")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline budget (0 disables)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 launches) to calibrate the "
+                         "FETCH_SIZE / WRITE_SIZE counters, then exit")
+    ap.add_argument("--traffic-json", default=None,
+                    help="JSON file with measured HBM bytes per forward launch ({'fetch_bytes': F, "
+                         "'write_bytes': W}) to report as roofline.traffic")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -104,10 +110,19 @@ def main():
     if not torch.cuda.is_available():
         print("no HIP device visible", file=sys.stderr)
         sys.exit(1)
-    p = inputs.PRESETS[args.preset]
-    passes = [x for x in args.passes.split(",") if x]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.arange(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3}), flush=True)
+        return
+    p = inputs.PRESETS[args.preset]
+    passes = [x for x in args.passes.split(",") if x]
 
     q, k, v, do = (t.to(dev) for t in inputs.make_preset(p, with_grad=True))
     o, lse = fwd(q, k, v, scale=p.scale, causal=p.causal)
@@ -167,19 +182,40 @@ def main():
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
     bwd_tflops = 2.5 * fwd_flops / (bwd_avg * 1e-3) / 1e12 if "bwd" in passes else None
 
-    # Dominant kernel for the roofline: the forward kernel (one launch per
-    # fa_fwd call), bound by bf16 MFMA throughput.
+    # Roofline of the forward kernel (one launch per fa_fwd call, so HIP
+    # events around the call time exactly that kernel), bound by bf16 MFMA
+    # throughput; the backward pass (three kernels per fa_bwd call) is given
+    # as a whole in roofline_bwd.
+    fwd_kernel = ("fwd_pp_kernel" if p.d in (64, 128) else "fwd_bf16_kernel") if p.dtype == "bf16" else "fwd_f32_kernel"
     roofline = {
         "bound": "mfma",
-        "kernel": "fwd_bf16_kernel<%d,%s>" % (p.d, "true" if p.causal else "false"),
+        "kernel": "%s<%d,%s>" % (fwd_kernel, p.d, "true" if p.causal else "false"),
         "achieved": round(fwd_tflops, 2) if fwd_tflops else None,
         "peak": round(PEAK_BF16_TFLOPS, 1),
         "unit": "TFLOP/s",
         "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
-        "traffic": None,
+        "traffic": None,  # filled from --traffic-json when counters were taken
         "avg_launch_ms": round(fwd_avg, 5),
         "alg_hbm_gbs": round(alg_bytes_fwd(p) / (fwd_avg * 1e-3) / 1e9, 1),
     }
+    roofline_bwd = None
+    if "bwd" in passes:
+        roofline_bwd = {
+            "bound": "mfma",
+            "kernels": "bwd_pre + bwd_dkdv + bwd_dq (one fa_bwd call)",
+            "achieved": round(bwd_tflops, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "avg_call_ms": round(bwd_avg, 5),
+            "flop_convention": "2.5 x forward",
+        }
+    if args.traffic_json:
+        with open(args.traffic_json) as f:
+            t = json.load(f)
+        roofline["traffic"] = {"fetch_bytes": t["fetch_bytes"], "write_bytes": t["write_bytes"],
+                               "total_bytes": t["fetch_bytes"] + t["write_bytes"],
+                               "alg_bytes": alg_bytes_fwd(p), "source": t.get("source", "")}
     line = {
         "metric": "attention fwd/bwd TFLOP/s (bf16, causal, d=128, N=2K-8K) + % MFMA peak",
         "value": round(value, 2),
@@ -207,6 +243,7 @@ def main():
         "peak_inputs": {"cus": torch.cuda.get_device_properties(dev).multi_processor_count, "sclk_ghz": 2.4,
                         "flop_per_clk_per_cu": 4096},
         "roofline": roofline,
+        "roofline_bwd": roofline_bwd,
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(p, passes, args.cpu_seconds)

@@ -27,7 +27,11 @@ def hipcc():
 
 
 def common_flags():
-    return [
+    # FA_EXTRA_DEFINES: optional build-time tile-configuration overrides
+    # (e.g. "FA_FWD_CFG128=2"), used for tile sweeps.
+    extra = [f"-D{x}" for x in os.environ.get("FA_EXTRA_DEFINES", "").split() if x]
+    extra += [x for x in os.environ.get("FA_EXTRA_FLAGS", "").split() if x]
+    return [*extra,
         f"--offload-arch={ARCH}",
         "-O3",
         "-fPIC",
@@ -50,7 +54,7 @@ def _compile(src):
     return obj, r.stderr
 
 
-def build(verbose=False):
+def build(verbose=False, out=None):
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         results = list(ex.map(_compile, SOURCES))
@@ -60,15 +64,16 @@ def build(verbose=False):
             f.write(f"==== {src}\n")
             f.write("\n".join(line for line in log.splitlines() if "remark" in line or "warning" in line.lower()))
             f.write("\n")
-    tmp = LIB + ".tmp"
+    target = out or LIB
+    tmp = target + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, target)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {target}")
+    return target
 
 
 if __name__ == "__main__":

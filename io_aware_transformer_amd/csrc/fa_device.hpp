@@ -113,6 +113,34 @@ template <int D>
 __device__ __forceinline__ int off_both(int r, int e) {
     return r * D + (swz_both<D>(r, e >> 3) << 3) + (e & 7);
 }
+// Slab layouts (every fragment a fixed offset from one per-lane base, so LDS
+// reads take immediate offsets instead of per-fragment address registers):
+//  K slabs: a ROWS x D tile as D/16 slabs of ROWS x 16 elements; within a
+//    32-byte row the two 16-byte halves are swapped when bit 3 of the row is
+//    set, so 16 consecutive rows of one half land in 16 distinct bank slots.
+//  V slabs: D/32 slabs of ROWS x 32 elements, rows of 64 bytes: a transpose
+//    read of 4 rows x 64 bytes covers all 64 banks exactly once.
+template <int ROWS>
+__device__ __forceinline__ int kslab_off(int r, int e) {
+    return (e >> 4) * ROWS * 16 + r * 16 + 8 * (((e >> 3) & 1) ^ ((r >> 3) & 1)) + (e & 7);
+}
+template <int ROWS>
+__device__ __forceinline__ int vslab_off(int r, int e) {
+    return (e >> 5) * ROWS * 32 + r * 32 + (e & 31);
+}
+// Inverse maps: 16-byte slot s of the tile -> (row, first element of the chunk).
+template <int ROWS>
+__device__ __forceinline__ void kslab_slot(int s, int& r, int& e0) {
+    const int cc = s / (2 * ROWS), rem = s - cc * 2 * ROWS;
+    r = rem >> 1;
+    e0 = 16 * cc + 8 * ((rem & 1) ^ ((r >> 3) & 1));
+}
+template <int ROWS>
+__device__ __forceinline__ void vslab_slot(int s, int& r, int& e0) {
+    const int db = s / (4 * ROWS), rem = s - db * 4 * ROWS;
+    r = rem >> 2;
+    e0 = 32 * db + 8 * (rem & 3);
+}
 // Element offset of (row r, element e) in a row-read tile.
 template <int D>
 __device__ __forceinline__ int off_row(int r, int e) {

@@ -11,20 +11,24 @@
 // Work decomposition ("The Future of AI: How FlashAttention Revolutionizes
 // Deep Learning", "FlashAttention-2: Enhanced Performance": parallel over
 // sequence length as well as batch and heads; queries split across warps
-// while keys/values are shared): one workgroup of 4 waves per
-// (batch, query head, block of 128 query rows); each wave owns 32 query
-// rows; K/V tiles of BN keys are staged in LDS (double-buffered through
-// registers) and read by all four waves.
+// while keys/values are shared): one workgroup of NW waves per
+// (batch, query head, block of BM = 32*QR*NW query rows); each wave owns
+// QR blocks of 32 query rows; K/V tiles of BN keys are copied global->LDS
+// by the direct-to-LDS load path (no VGPR staging), multi-buffered, and
+// read by every wave.  With QR = 2 every K/V fragment read from LDS feeds two
+// matrix products, halving LDS traffic per FLOP.
 //
-// Per wave and 32-key block, in the layouts of fa_device.hpp:
+// Per wave, row block and 32-key block, in the layouts of fa_device.hpp:
 //   S^T (32 keys x 32 queries) = K_blk . Q^T     A = K rows (LDS), B = Q (regs)
 //   lane l then holds one query (l % 32) and 16 of its keys, so the row
 //   max/sum are in-lane plus one v_permlane32_swap across the halves.
 //   O^T (d x 32 queries) += V^T . P^T            A = V^T via ds_read_b64_tr_b16,
 //   B = P^T straight from the score registers (the key order inside the
 //   contraction is permuted consistently on both operands).
-// Scores are scaled by scale*log2(e) so the exponentials are exp2 (v_exp_f32);
-// LSE is converted back to natural log at the end.
+// Scores are scaled by c = |scale|*log2(e) so the exponentials are exp2
+// (v_exp_f32) and p = exp2(c*s - m) is one FMA; LSE is converted back to a
+// natural log at the end.  A negative scale is handled by negating Q (exact
+// in bf16), a zero scale by zeroing Q, so the kernel only sees c > 0.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -34,27 +38,52 @@ namespace fa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+// Tile configuration per head dim: waves per workgroup (each wave owns 32
+// query rows), keys per tile, LDS stages, waves per SIMD the register
+// budget is cut for.
+template <int D>
+struct FwdCfg;
+#ifndef FA_FWD_BN128
+#define FA_FWD_BN128 64
+#endif
+#ifndef FA_FWD_BN64
+#define FA_FWD_BN64 64
+#endif
+#ifndef FA_FWD_NW
+#define FA_FWD_NW 4
+#endif
+template <int NW_, int BN_, int NST_, int WPE_>
+struct FwdCfgT {
+    static constexpr int NW = NW_, BN = BN_, NST = NST_, WPE = WPE_;
+};
+template <>
+struct FwdCfg<64> : FwdCfgT<FA_FWD_NW, FA_FWD_BN64, 2, 2> {};
+template <>
+struct FwdCfg<128> : FwdCfgT<FA_FWD_NW, FA_FWD_BN128, 2, 2> {};
+template <>
+struct FwdCfg<256> : FwdCfgT<4, 32, 2, 1> {};
+
+// Rescale threshold in log2 units.  0: the running max follows the row max
+// exactly (the recurrence as stated; factors of exactly 1 are skipped).
+// > 0: the reference max is only moved when the row max exceeds it by more
+// than kTau, so exponentials stay <= 2^kTau and the result is unchanged.
+#ifndef FA_FWD_TAU
+#define FA_FWD_TAU 0.0f
+#endif
+constexpr float kTau = FA_FWD_TAU;
+
+// 1: d = 64 / 128 use the ping-pong kernel below; 0: the single-group kernel.
+#ifndef FA_FWD_PP
+#define FA_FWD_PP 1
+#endif
 
 template <int D>
-struct FwdTile;
-template <>
-struct FwdTile<64> {
-    static constexpr int BN = 64;
-};
-template <>
-struct FwdTile<128> {
-    static constexpr int BN = 64;
-};
-template <>
-struct FwdTile<256> {
-    static constexpr int BN = 32;
-};
-
+constexpr int fwd_bm() {
+    return 32 * FwdCfg<D>::NW;
+}
 template <int D>
 constexpr size_t fwd_lds_bytes() {
-    return size_t(2) /*stages*/ * 2 /*K,V*/ * FwdTile<D>::BN * D * sizeof(bf16);
+    return size_t(FwdCfg<D>::NST) * 2 /*K,V*/ * FwdCfg<D>::BN * D * sizeof(bf16);
 }
 
 // Workgroup id -> (query block, batch, head).  Heaviest causal query blocks
@@ -71,19 +100,94 @@ __device__ __forceinline__ void fwd_decompose(int id, int units, int nqb, int Hq
     h = unit - b * Hq;
 }
 
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer, gfx9 descriptor
+// word 3 = 0x00020000).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16-byte buffer load straight into LDS: lane l writes dst_uniform + 16 l.
+__device__ __forceinline__ void buf16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, bf16* dst_uniform) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst_uniform, 16, voff, 0, 0, 0);
+#pragma clang diagnostic pop
+}
+
+// Wait for this wave's outstanding global loads (including direct-to-LDS
+// copies): s_waitcnt vmcnt(0) with expcnt/lgkmcnt left at their maximum.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// K/V tiles are copied global -> LDS by the direct-to-LDS load path (no
+// VGPR staging) in 1 KB pieces, one per wave instruction: lane l of piece p
+// writes 16-byte slot 64p + l and fetches the chunk that the tile's slab
+// layout (K slabs / V slabs, fa_device.hpp) places in that slot.  Each copy
+// goes through a buffer resource whose base is the first row of the tile,
+// so a lane's byte offset is the same for every tile.  On the tail tile,
+// rows at or past N are clamped to row N-1 (read in bounds, masked later).
+template <int D, int BN, int NW>
+struct TileCopy {
+    static constexpr int PIECES = BN * D * 2 / 1024;
+    static constexpr int PER_WAVE = PIECES / NW;
+    static_assert(PIECES % NW == 0, "tile pieces must split evenly over the waves");
+    // In-tile byte offset (2 * (row * D + first element)) of each piece this lane copies.
+    uint32_t koff[PER_WAVE], voff[PER_WAVE];
+    int piece0;  // first piece of this wave (uniform)
+
+    __device__ __forceinline__ void init(int w, int lane) {
+        piece0 = w;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int s = (w + NW * i) * 64 + lane;
+            int r, e0;
+            kslab_slot<BN>(s, r, e0);
+            koff[i] = uint32_t(2 * (r * D + e0));
+            vslab_slot<BN>(s, r, e0);
+            voff[i] = uint32_t(2 * (r * D + e0));
+        }
+    }
+    __device__ __forceinline__ void issue(const bf16* Kh, const bf16* Vh, bf16* Ks, bf16* Vs, int key0, int N) const {
+        const uint32_t bytes = uint32_t(N - key0) * uint32_t(D * 2);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kh + size_t(key0) * D, bytes);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vh + size_t(key0) * D, bytes);
+        if (key0 + BN <= N) {
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) {
+                const int piece = piece0 + NW * i;
+                buf16_to_lds(kr, koff[i], Ks + piece * 512);
+                buf16_to_lds(vr, voff[i], Vs + piece * 512);
+            }
+        } else {
+            const uint32_t last = uint32_t(N - 1 - key0);  // last valid row of the tile
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) {
+                const int piece = piece0 + NW * i;
+                const uint32_t rk = koff[i] / (2 * D), rv = voff[i] / (2 * D);
+                const uint32_t ok = min(rk, last) * (2 * D) + koff[i] % (2 * D);
+                const uint32_t ov = min(rv, last) * (2 * D) + voff[i] % (2 * D);
+                buf16_to_lds(kr, ok, Ks + piece * 512);
+                buf16_to_lds(vr, ov, Vs + piece * 512);
+            }
+        }
+    }
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
-    constexpr int BN = FwdTile<D>::BN;
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
+__global__ __launch_bounds__(FwdCfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE)))
+void fwd_bf16_kernel(FwdParams p) {
+    constexpr int NW = FwdCfg<D>::NW, BN = FwdCfg<D>::BN, NST = FwdCfg<D>::NST;
+    constexpr int BM = 32 * NW;
     constexpr int TILE = BN * D;
-    constexpr int NLD = BN * CPR / 256;  // chunks per thread per tile and matrix
-    static_assert(NLD >= 1 && (BN * CPR) % 256 == 0, "tile must split evenly over 256 threads");
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    constexpr int KB = BN / 32;
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
     bf16* smem = reinterpret_cast<bf16*>(smem_raw);
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+    const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const int N = p.N;
+    const float c = p.scale_log2;  // > 0
 
     int qb, b, h;
     fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, qb, b, h);
@@ -95,132 +199,131 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
     bf16* __restrict__ Oh = static_cast<bf16*>(p.O) + qoff;
 
-    const int q0 = qb * kBM;
-    const int wq0 = q0 + 32 * w;  // first query row of this wave
-    const int qrow = wq0 + l32;   // the query row this lane works for
+    const int q0 = qb * BM;
+    const int wq0 = q0 + 32 * w;  // first query row of this wave (uniform)
+    const int wq_last = wq0 + 31;
+    const int qrow = wq0 + l32;   // the query row of this lane
 
-    // Q tile of this wave as the MFMA B operand: Q[qrow][16c + 8hi .. +7].
-    bf16x8 qreg[D / 16];
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-        if (qrow < N) qreg[c] = as_bf16x8(ld16(Qh + size_t(qrow) * D + 16 * c + 8 * hi));
-        else qreg[c] = bf16x8{};
-    }
-
-    const int kend = CAUSAL ? min(N, q0 + kBM) : N;
+    const int kend = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kend + BN - 1) / BN;
 
-    u32x4 kpre[NLD], vpre[NLD];
-    auto gload = [&](int kt) {
+    TileCopy<D, BN, NW> cp;
+    cp.init(w, lane);
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / CPR, c = idx % CPR;
-            const int key = kt * BN + r;
-            if (key < N) {
-                kpre[i] = ld16(Kh + size_t(key) * D + 8 * c);
-                vpre[i] = ld16(Vh + size_t(key) * D + 8 * c);
-            } else {
-                kpre[i] = u32x4{0, 0, 0, 0};
-                vpre[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto lstore = [&](int stage) {
-        bf16* Ks = smem + stage * 2 * TILE;
-        bf16* Vs = Ks + TILE;
+    for (int st = 0; st < NST - 1; ++st)
+        if (st < ntiles) cp.issue(Kh, Vh, smem + st * 2 * TILE, smem + st * 2 * TILE + TILE, st * BN, N);
+
+    // Q rows of this wave as MFMA B operands: Q[qrow][16cc + 8hi .. +7].
+    // qmode 1 negates (negative scale), 2 zeroes (zero scale).
+    bf16x8 qreg[D / 16];
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / CPR, c = idx % CPR;
-            st16(Ks + r * D + 8 * swz_row<D>(r, c), kpre[i]);
-            st16(Vs + r * D + 8 * swz_tr<D>(r, c), vpre[i]);
-        }
-    };
+    for (int cc = 0; cc < D / 16; ++cc) {
+        u32x4 v = u32x4{0, 0, 0, 0};
+        if (qrow < N && p.qmode != 2) v = ld16(Qh + size_t(qrow) * D + 16 * cc + 8 * hi);
+        if (p.qmode == 1) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        qreg[cc] = as_bf16x8(v);
+    }
 
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    float m = -INFINITY;  // running max, in log2 units of the scaled scores
-    float l = 0.f;        // running sum of this lane's keys (halves merged at the end)
+    float m = -INFINITY;  // running (reference) max of c*s
+    float l = 0.f;        // running sum over this lane's keys (halves merged at the end)
+    const int trow = 4 * hi + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // Row limit for masking: keys above it are hidden (causal and/or past N).
+    const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
 
-    gload(0);
-    lstore(0);
+    wait_vmem();
     __syncthreads();
 
     for (int kt = 0; kt < ntiles; ++kt) {
-        const int stage = kt & 1;
-        if (kt + 1 < ntiles) gload(kt + 1);
-        const bf16* Ks = smem + stage * 2 * TILE;
+        {
+            const int nt = kt + NST - 1;
+            if (nt < ntiles) {
+                bf16* st = smem + (nt % NST) * 2 * TILE;
+                cp.issue(Kh, Vh, st, st + TILE, nt * BN, N);
+            }
+        }
+        const bf16* Ks = smem + (kt % NST) * 2 * TILE;
         const bf16* Vs = Ks + TILE;
         const int kstart = kt * BN;
 
-        if (!CAUSAL || kstart <= wq0 + 31) {
-            // S^T blocks: s[kb][r] = score(key = kstart + 32kb + 8(r/4) + 4hi + r%4, query = qrow)
-            f32x16 s[BN / 32];
+        if (!CAUSAL || kstart <= wq_last) {
+            // S^T blocks: s[kb][r] = score(key kstart + 32kb + 8(r/4) + 4hi + r%4, query qrow).
+            // The KB accumulation chains are interleaved so consecutive MFMAs are independent.
+            f32x16 s[KB];
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
-                s[kb] = f32x16{};
+            for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    const bf16x8 a = as_bf16x8(ld16(Ks + off_row<D>(kb * 32 + l32, 16 * c + 8 * hi)));
-                    s[kb] = mfma_32x32x16(a, qreg[c], s[kb]);
+            for (int cc = 0; cc < D / 16; ++cc) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    if (CAUSAL && kstart + 32 * kb > wq_last) continue;
+                    const bf16x8 a = as_bf16x8(ld16(Ks + kslab_off<BN>(kb * 32 + l32, 16 * cc + 8 * hi)));
+                    s[kb] = mfma_32x32x16(a, qreg[cc], s[kb]);
                 }
             }
             const bool need_mask = (CAUSAL && kstart + BN - 1 > wq0) || (kstart + BN > N);
+            if (need_mask) {
+                const int lim = key_lim - kstart - 4 * hi;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[kb][r];
+            }
             float mx = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float t = s[kb][r] * p.scale_log2;
-                    if (need_mask) {
-                        const int key = kstart + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        if ((CAUSAL && key > qrow) || key >= N) t = -INFINITY;
-                    }
-                    s[kb][r] = t;
-                    mx = fmaxf(mx, t);
-                }
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = half_swap_max(mx) * c;
+            // Rescale only when some row of this wave raised its max (by more
+            // than kTau): otherwise every factor exp(m_old - m_new) is exactly
+            // 1 and the multiply is skipped.  The branch is wave-uniform.
+            if (__any(mx > m + kTau)) {
+                const float m_new = fmaxf(m, mx);
+                const float alpha = fast_exp2(m - m_new);
+                m = m_new;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
             }
-            mx = half_swap_max(mx);
-            const float m_new = fmaxf(m, mx);
-            const float alpha = fast_exp2(m - m_new);
-            m = m_new;
+            bf16x8 pb[KB][2];
             float rs = 0.f;
-            bf16x8 pb[BN / 32][2];
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float e = fast_exp2(s[kb][r] - m_new);
+                    const float e = fast_exp2(fmaf(s[kb][r], c, -m));
                     s[kb][r] = e;
                     rs += e;
                 }
-                pb[kb][0] = to_bf16x8(s[kb][0], s[kb][1], s[kb][2], s[kb][3], s[kb][4], s[kb][5], s[kb][6], s[kb][7]);
-                pb[kb][1] = to_bf16x8(s[kb][8], s[kb][9], s[kb][10], s[kb][11], s[kb][12], s[kb][13], s[kb][14],
-                                      s[kb][15]);
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc)
+                    pb[kb][cc] = to_bf16x8(s[kb][8 * cc + 0], s[kb][8 * cc + 1], s[kb][8 * cc + 2], s[kb][8 * cc + 3],
+                                           s[kb][8 * cc + 4], s[kb][8 * cc + 5], s[kb][8 * cc + 6], s[kb][8 * cc + 7]);
             }
-            l = l * alpha + rs;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+            l += rs;
             // O^T += V^T P^T.  Contraction slot (cc, hi, sl) <-> key 32kb + 16cc + 8(sl/4) + 4hi + sl%4.
-            const int trow = 4 * hi + ((lane & 15) >> 2);
-            const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            // Consecutive MFMAs update different dim blocks (independent accumulators).
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
+            for (int kb = 0; kb < KB; ++kb) {
+                if (CAUSAL && kstart + 32 * kb > wq_last) continue;
 #pragma unroll
-                for (int kb = 0; kb < BN / 32; ++kb) {
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int key = kb * 32 + 16 * cc + trow;
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) {
-                        const int key = kb * 32 + 16 * cc + trow;
-                        const bf16x4 v0 = lds_read_tr(Vs + off_tr<D>(key, db * 32 + tcol));
-                        const bf16x4 v1 = lds_read_tr(Vs + off_tr<D>(key + 8, db * 32 + tcol));
+                    for (int db = 0; db < D / 32; ++db) {
+                        const bf16x4 v0 = lds_read_tr(Vs + vslab_off<BN>(key, db * 32 + tcol));
+                        const bf16x4 v1 = lds_read_tr(Vs + vslab_off<BN>(key + 8, db * 32 + tcol));
                         o[db] = mfma_32x32x16(cat(v0, v1), pb[kb][cc], o[db]);
                     }
                 }
             }
         }
-        if (kt + 1 < ntiles) lstore(stage ^ 1);
+        wait_vmem();
         __syncthreads();
     }
 
@@ -242,6 +345,332 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong forward (d = 64, 128).  Two waves share every SIMD; if both ran
+// the same phase (matrix products, then softmax) at the same time, the
+// matrix cores would idle during the softmax.  Here the 8 waves of a
+// workgroup form two groups of 4 (one wave of each group per SIMD) that run
+// the same software pipeline one phase apart:
+//   M phase j:  O^T += V_{j-1}^T P_{j-1}^T   and   S_j^T = K_j Q^T   (MFMA)
+//   V phase j:  softmax of S_j (max, rescale, exp2, sum, bf16 P_j)   (VALU)
+// While group A is in an M phase, group B is in a V phase and vice versa;
+// a workgroup barrier closes every phase and keeps the offset.  K/V tiles
+// are triple-buffered in LDS: tile j is read from A's M phase j to B's M
+// phase j+1, and tile j+3 is copied into its buffer two phases before it is
+// first needed.  Group A owns query rows q0 .. q0+127, group B q0+128 ..
+// q0+255.
+// ---------------------------------------------------------------------------
+template <int D>
+struct PPCfg;
+template <>
+struct PPCfg<64> {
+    static constexpr int BN = FA_FWD_BN64;
+};
+template <>
+struct PPCfg<128> {
+    static constexpr int BN = FA_FWD_BN128;
+};
+constexpr int kPPWaves = 8;
+constexpr int kPPStages = 3;
+constexpr int kPPBM = 32 * kPPWaves;
+
+template <int D>
+constexpr size_t pp_lds_bytes() {
+    // K/V stages plus two V^T buffers
+    return (size_t(kPPStages) * 2 + 2) * PPCfg<D>::BN * D * sizeof(bf16);
+}
+
+// V^T tile layout: element (dim, key) of a D x BN tile.  Keys are grouped
+// by 16; inside a group the order is [4hi+0..3, 8+4hi+0..3] for hi = 0, 1,
+// which is the key order of the MFMA A operand, so one 16-byte read gives a
+// lane its 8 keys; the two 16-byte halves of a row are swapped when bit 3
+// of the dim is set (conflict-free reads of 16 consecutive dims).
+template <int D>
+__device__ __forceinline__ int vt_off(int dim, int key) {
+    return (key >> 4) * D * 16 + dim * 16 + 8 * (((key >> 2) & 1) ^ ((dim >> 3) & 1)) + 4 * ((key >> 3) & 1) +
+           (key & 3);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kPPWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_pp_kernel(FwdParams p) {
+    constexpr int BN = PPCfg<D>::BN;
+    constexpr int NST = kPPStages;
+    constexpr int BM = kPPBM;
+    constexpr int TILE = BN * D;
+    constexpr int KB = BN / 32;
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+    bf16* smem = reinterpret_cast<bf16*>(smem_raw);
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+    const int grp = w >> 2;                                  // 0: group A, 1: group B
+    const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int N = p.N;
+    const float c = p.scale_log2;  // > 0
+
+    int qb, b, h;
+    fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, qb, b, h);
+    const int g = h / (p.Hq / p.Hkv);
+    const size_t qoff = size_t(b * p.Hq + h) * size_t(N) * D;
+    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const bf16* __restrict__ Qh = static_cast<const bf16*>(p.Q) + qoff;
+    const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
+    const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
+    bf16* __restrict__ Oh = static_cast<bf16*>(p.O) + qoff;
+
+    const int q0 = qb * BM;
+    const int wq0 = q0 + 32 * w;  // first query row of this wave (uniform)
+    const int wq_last = wq0 + 31;
+    const int qrow = wq0 + l32;
+
+    const int kend = CAUSAL ? min(N, q0 + BM) : N;
+    const int T = (kend + BN - 1) / BN;  // tiles of the workgroup
+
+    TileCopy<D, BN, kPPWaves> cp;
+    cp.init(w, lane);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+        if (t < T) cp.issue(Kh, Vh, smem + t * 2 * TILE, smem + t * 2 * TILE + TILE, t * BN, N);
+
+    bf16x8 qreg[D / 16];
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+        u32x4 v = u32x4{0, 0, 0, 0};
+        if (qrow < N && p.qmode != 2) v = ld16(Qh + size_t(qrow) * D + 16 * cc + 8 * hi);
+        if (p.qmode == 1) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        qreg[cc] = as_bf16x8(v);
+    }
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    f32x16 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+    bf16x8 pb[KB][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) pb[kb][0] = pb[kb][1] = bf16x8{};
+    float m = -INFINITY, l = 0.f;
+    const int trow = 4 * hi + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+
+    // Number of 32-key blocks of tile j this wave must process (uniform).
+    auto active_kb = [&](int j) -> int {
+        if (!CAUSAL) return KB;
+        const int kstart = j * BN;
+        if (kstart > wq_last) return 0;
+        return min(KB, (wq_last - kstart) / 32 + 1);
+    };
+
+    wait_vmem();
+    __syncthreads();
+
+    // Per-lane element offset of the V^T A-operand read (dim l32 of a 32-dim
+    // block, the 8 keys of half hi of a 16-key group).
+    const int vt_lane = vt_off<D>(l32, 4 * hi);
+    // Transpose tile j's V (V slabs) into V^T buffer j % 2.  Done by the 4
+    // waves of group A in their V phase; each transposing read returns 4
+    // consecutive keys of one dim, written back as one 8-byte store.
+    constexpr int TR_PER_WAVE = (BN / 8) * (D / 32) / 4;
+    auto transpose_v = [&](int j, bf16x4 (&buf)[TR_PER_WAVE], bool write) {
+        const bf16* Vs = smem + (j % NST) * 2 * TILE + TILE;
+        bf16* VT = smem + (2 * NST + (j & 1)) * TILE;
+#pragma unroll
+        for (int i = 0; i < TR_PER_WAVE; ++i) {
+            const int t = w + 4 * i;  // instruction index 0 .. (BN/8)(D/32) - 1
+            const int kb8 = t / (D / 32), db = t - (t / (D / 32)) * (D / 32);
+            if (!write) {
+                buf[i] = lds_read_tr(Vs + vslab_off<BN>(8 * kb8 + trow, db * 32 + tcol));
+            } else {
+                *reinterpret_cast<bf16x4*>(VT + vt_off<D>(db * 32 + l32, 8 * kb8 + 4 * hi)) = buf[i];
+            }
+        }
+    };
+
+    // Steps 0 .. 2T+1, one workgroup barrier after each.  Group A: step 2j is
+    // its M phase j, step 2j+1 its V phase j.  Group B runs one step later.
+    // K/V refill: at even step 2t-2 (t >= 3) tile t goes into the buffer of
+    // tile t-3, whose last reader (group B, M phase t-2) finished in the
+    // previous step; the copy is waited for at the end of the next (odd) step.
+    auto refill = [&](int step) {
+        if (!(step & 1) && step >= 4) {
+            const int t = step / 2 + 1;
+            if (t < T) {
+                bf16* st = smem + (t % NST) * 2 * TILE;
+                cp.issue(Kh, Vh, st, st + TILE, t * BN, N);
+            }
+        }
+    };
+    auto finish = [&](int step) {
+        if ((step & 1) && step >= 5) wait_vmem();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_s_barrier();
+    };
+    // ---- M phase j: PV of tile j-1, then QK of tile j.  LDS fragments are
+    // loaded one block ahead of the MFMAs that use them; scheduling barriers
+    // keep at most two blocks live.
+    auto phase_m = [&](int j) {
+        if (j >= 1 && active_kb(j - 1) > 0) {
+            // V^T of tile j-1 (written by group A in its V phase j-1): one
+            // 16-byte read per A operand.
+            const bf16* VT = smem + (2 * NST + ((j - 1) & 1)) * TILE + vt_lane;
+            bf16x8 fa[D / 32], fb[D / 32];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) fa[db] = as_bf16x8(ld16(VT + db * 32 * 16));
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) fb[db] = as_bf16x8(ld16(VT + (2 * kb + 1) * D * 16 + db * 32 * 16));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x16(fa[db], pb[kb][0], o[db]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kb + 1 < KB) {
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+                        fa[db] = as_bf16x8(ld16(VT + (2 * kb + 2) * D * 16 + db * 32 * 16));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x16(fb[db], pb[kb][1], o[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (j < T && active_kb(j) > 0) {
+            const bf16* Ks = smem + (j % NST) * 2 * TILE;
+            bf16x8 ka[KB], kbf[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                s[kb] = f32x16{};
+                ka[kb] = as_bf16x8(ld16(Ks + kslab_off<BN>(kb * 32 + l32, 8 * hi)));
+            }
+#pragma unroll
+            for (int cc = 0; cc < D / 16; cc += 2) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    kbf[kb] = as_bf16x8(ld16(Ks + kslab_off<BN>(kb * 32 + l32, 16 * (cc + 1) + 8 * hi)));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) s[kb] = mfma_32x32x16(ka[kb], qreg[cc], s[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (cc + 2 < D / 16) {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        ka[kb] = as_bf16x8(ld16(Ks + kslab_off<BN>(kb * 32 + l32, 16 * (cc + 2) + 8 * hi)));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) s[kb] = mfma_32x32x16(kbf[kb], qreg[cc + 1], s[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    // ---- V phase j: online softmax of S_j -> P_j (bf16), O rescaled if needed.
+    auto phase_v = [&](int j) {
+        if (j >= T || active_kb(j) == 0) return;
+        const int kstart = j * BN;
+        const bool need_mask = (CAUSAL && kstart + BN - 1 > wq0) || (kstart + BN > N);
+        if (need_mask) {
+            const int lim = key_lim - kstart - 4 * hi;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[kb][r];
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = half_swap_max(mx) * c;
+        if (__any(mx > m + kTau)) {
+            const float m_new = fmaxf(m, mx);
+            const float alpha = fast_exp2(m - m_new);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float e[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                e[r] = fast_exp2(fmaf(s[kb][r], c, -m));
+                rs += e[r];
+            }
+            pb[kb][0] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+            pb[kb][1] = to_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+        }
+        l += rs;
+    };
+
+    if (grp == 0) {
+        for (int j = 0; j <= T; ++j) {
+            refill(2 * j);
+            phase_m(j);
+            finish(2 * j);
+            refill(2 * j + 1);
+            if (j < T) {
+                bf16x4 tb[TR_PER_WAVE];
+                transpose_v(j, tb, false);
+                phase_v(j);
+                transpose_v(j, tb, true);
+            }
+            finish(2 * j + 1);
+        }
+    } else {
+        finish(0);
+        for (int j = 0; j <= T; ++j) {
+            refill(2 * j + 1);
+            phase_m(j);
+            finish(2 * j + 1);
+            if (j < T) {
+                refill(2 * j + 2);
+                phase_v(j);
+                finish(2 * j + 2);
+            }
+        }
+    }
+
+    const float lt = half_swap_sum(l);
+    const float inv = 1.f / lt;
+    if (qrow < N) {
+        bf16* orow = Oh + size_t(qrow) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const bf16x4 v = bf16x4{(bf16)(o[db][4 * jj + 0] * inv), (bf16)(o[db][4 * jj + 1] * inv),
+                                        (bf16)(o[db][4 * jj + 2] * inv), (bf16)(o[db][4 * jj + 3] * inv)};
+                *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * jj + 4 * hi) = v;
+            }
+        }
+        if (hi == 0 && p.LSE != nullptr) p.LSE[size_t(b * p.Hq + h) * N + qrow] = (m + fast_log2(lt)) * kLn2;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_pp_t(FwdParams p, hipStream_t stream) {
+    auto kern = fwd_pp_kernel<D, CAUSAL>;
+    constexpr size_t lds = pp_lds_bytes<D>();
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    p.nqb = (p.N + kPPBM - 1) / kPPBM;
+    const long long blocks = (long long)p.nqb * p.B * p.Hq;
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kPPWaves * 64), lds, stream, p);
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
     auto kern = fwd_bf16_kernel<D, CAUSAL>;
@@ -253,18 +682,322 @@ hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    p.nqb = (p.N + kBM - 1) / kBM;
+    constexpr int BM = fwd_bm<D>();
+    p.nqb = (p.N + BM - 1) / BM;
     const long long blocks = (long long)p.nqb * p.B * p.Hq;
-    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), lds, stream, p);
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(FwdCfg<D>::NW * 64), lds, stream, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Two-row-block forward (d = 64, 128).  gfx950 LDS delivers about 128 bytes
+// per clock per CU, which is what the matrix cores consume when every
+// 32x32x16 product reads a fresh 1 KB K or V fragment; here each wave owns
+// 64 query rows (two 32-row blocks), so every fragment read from LDS feeds
+// two products and LDS traffic per FLOP halves.  The price is one wave per
+// SIMD, so the softmax has to overlap the matrix products inside the wave:
+// iteration j issues, as one straight-line block,
+//     QK_j (both row blocks)  ->  PV_{j-1} (both row blocks)  ->  softmax_j
+// The softmax of tile j reads S_j and writes P_j while the PV products of
+// tile j-1 are still in flight.  A rescale of O needed by tile j (only when
+// a row max grew) is applied at the top of iteration j+1, before PV_j, so
+// the block stays branch-free.  K/V tiles are 4-buffered in LDS (direct
+// loads, K slabs / V slabs), issued two iterations ahead.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Qr2Cfg;
+template <>
+struct Qr2Cfg<64> {
+    static constexpr int BN = 64;
+};
+template <>
+struct Qr2Cfg<128> {
+    static constexpr int BN = 32;
+};
+constexpr int kQr2Waves = 4;
+constexpr int kQr2Stages = 4;
+constexpr int kQr2BM = 64 * kQr2Waves;
+
+template <int D>
+constexpr size_t qr2_lds_bytes() {
+    return size_t(kQr2Stages) * 2 * Qr2Cfg<D>::BN * D * sizeof(bf16);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kQr2Waves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_qr2_kernel(FwdParams p) {
+    constexpr int BN = Qr2Cfg<D>::BN;
+    constexpr int NST = kQr2Stages;
+    constexpr int BM = kQr2BM;
+    constexpr int TILE = BN * D;
+    constexpr int KB = BN / 32;
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+    bf16* smem = reinterpret_cast<bf16*>(smem_raw);
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int N = p.N;
+    const float c = p.scale_log2;  // > 0
+
+    int qb, b, h;
+    fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, qb, b, h);
+    const int g = h / (p.Hq / p.Hkv);
+    const size_t qoff = size_t(b * p.Hq + h) * size_t(N) * D;
+    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const bf16* __restrict__ Qh = static_cast<const bf16*>(p.Q) + qoff;
+    const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
+    const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
+    bf16* __restrict__ Oh = static_cast<bf16*>(p.O) + qoff;
+
+    const int q0 = qb * BM;
+    const int wq0 = q0 + 64 * w;  // first query row of this wave (uniform)
+    const int wq_last = wq0 + 63;
+
+    const int kend = CAUSAL ? min(N, q0 + BM) : N;
+    const int T = (kend + BN - 1) / BN;
+
+    TileCopy<D, BN, kQr2Waves> cp;
+    cp.init(w, lane);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        if (t < T) cp.issue(Kh, Vh, smem + t * 2 * TILE, smem + t * 2 * TILE + TILE, t * BN, N);
+
+    bf16x8 qreg[2][D / 16];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = wq0 + 32 * rb + l32;
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+            u32x4 v = u32x4{0, 0, 0, 0};
+            if (row < N && p.qmode != 2) v = ld16(Qh + size_t(row) * D + 16 * cc + 8 * hi);
+            if (p.qmode == 1) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+            qreg[rb][cc] = as_bf16x8(v);
+        }
+    }
+
+    f32x16 o[2][D / 32];
+    float m[2], l[2], alpha[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[rb][db] = f32x16{};
+        m[rb] = -INFINITY;
+        l[rb] = 0.f;
+        alpha[rb] = 1.f;
+    }
+    bool pending = false;  // O must be rescaled by alpha before the next PV
+    bf16x8 pb[2][KB][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) pb[rb][kb][0] = pb[rb][kb][1] = bf16x8{};
+
+    const int trow = 4 * hi + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int kq_lane = kslab_off<BN>(l32, 8 * hi);      // K A-operand base (elements)
+    const int vt_lane = vslab_off<BN>(trow, tcol);        // V transpose-read base
+    int key_lim[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = wq0 + 32 * rb + l32;
+        key_lim[rb] = CAUSAL ? min(row, N - 1) : N - 1;
+    }
+
+    auto active = [&](int j) -> bool { return !CAUSAL || j * BN <= wq_last; };
+
+    // QK of tile j for both row blocks: every K fragment feeds two MFMAs.
+    auto qk = [&](int j, f32x16 (&s)[2][KB]) {
+        const bf16* Ks = smem + (j % NST) * 2 * TILE + kq_lane;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) s[rb][kb] = f32x16{};
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 a = as_bf16x8(ld16(Ks + cc * BN * 16 + kb * 32 * 16));
+                s[0][kb] = mfma_32x32x16(a, qreg[0][cc], s[0][kb]);
+                s[1][kb] = mfma_32x32x16(a, qreg[1][cc], s[1][kb]);
+            }
+        }
+    };
+    // PV of tile j with the P held in pb: every V fragment feeds two MFMAs.
+    auto pv = [&](int j) {
+        const bf16* Vs = smem + (j % NST) * 2 * TILE + TILE + vt_lane;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const bf16x4 v0 = lds_read_tr(Vs + db * BN * 32 + (kb * 32 + 16 * cc) * 32);
+                    const bf16x4 v1 = lds_read_tr(Vs + db * BN * 32 + (kb * 32 + 16 * cc + 8) * 32);
+                    const bf16x8 a = cat(v0, v1);
+                    o[0][db] = mfma_32x32x16(a, pb[0][kb][cc], o[0][db]);
+                    o[1][db] = mfma_32x32x16(a, pb[1][kb][cc], o[1][db]);
+                }
+            }
+        }
+    };
+    // Online softmax of tile j for both row blocks -> pb, alpha, pending.
+    auto softmax = [&](int j, f32x16 (&s)[2][KB], bool need_mask) {
+        const int kstart = j * BN;
+        bool grow = false;
+        float mnew[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            if (need_mask) {
+                const int lim = key_lim[rb] - kstart - 4 * hi;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        s[rb][kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[rb][kb][r];
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
+            mx = half_swap_max(mx) * c;
+            grow = grow || (mx > m[rb] + kTau);
+            mnew[rb] = fmaxf(m[rb], mx);
+        }
+        const bool any_grow = __any(grow);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const float mr = any_grow ? mnew[rb] : m[rb];
+            alpha[rb] = fast_exp2(m[rb] - mr);
+            m[rb] = mr;
+            float rs = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                float e[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    e[r] = fast_exp2(fmaf(s[rb][kb][r], c, -mr));
+                    rs += e[r];
+                }
+                pb[rb][kb][0] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+                pb[rb][kb][1] = to_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+            }
+            l[rb] = l[rb] * alpha[rb] + rs;
+        }
+        pending = any_grow;
+    };
+
+    wait_vmem();
+    __syncthreads();
+
+    // Iteration j: [rescale O if tile j-1 raised a max] QK_j, PV_{j-1}, softmax_j.
+    // Tile t is copied at iteration t-2 into the buffer of tile t-4 (last read
+    // by PV_{t-4} in iteration t-3) and waited for at the end of iteration t-1.
+    for (int j = 0; j <= T; ++j) {
+        if (j + 2 < T) {
+            const int t = j + 2;
+            bf16* st = smem + (t % NST) * 2 * TILE;
+            cp.issue(Kh, Vh, st, st + TILE, t * BN, N);
+        }
+        if (pending) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o[rb][db] *= alpha[rb];
+            pending = false;
+        }
+        const bool do_qk = j < T && active(j);
+        const bool do_pv = j >= 1 && active(j - 1);
+        const bool need_mask = do_qk && ((CAUSAL && j * BN + BN - 1 > wq0) || (j * BN + BN > N));
+        f32x16 s[2][KB];
+        if (do_qk && do_pv && !need_mask) {
+            // steady state: one straight-line block
+            qk(j, s);
+            pv(j - 1);
+            softmax(j, s, false);
+        } else {
+            if (do_qk) qk(j, s);
+            if (do_pv) pv(j - 1);
+            if (do_qk) softmax(j, s, need_mask);
+        }
+        // tile j+1 (copied in iteration j-1) must be visible to every wave.
+        // vmcnt counts per wave in issue order: leaving the 2*PER_WAVE copies of
+        // tile j+2 outstanding would need a partial wait; waiting for all keeps
+        // it simple (tile j+2 has had the whole iteration to land).
+        wait_vmem();
+        __syncthreads();
+    }
+    if (pending) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[rb][db] *= alpha[rb];
+    }
+
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int qrow = wq0 + 32 * rb + l32;
+        const float lt = half_swap_sum(l[rb]);
+        const float inv = 1.f / lt;
+        if (qrow < N) {
+            bf16* orow = Oh + size_t(qrow) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const bf16x4 v = bf16x4{(bf16)(o[rb][db][4 * jj + 0] * inv), (bf16)(o[rb][db][4 * jj + 1] * inv),
+                                            (bf16)(o[rb][db][4 * jj + 2] * inv), (bf16)(o[rb][db][4 * jj + 3] * inv)};
+                    *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * jj + 4 * hi) = v;
+                }
+            }
+            if (hi == 0 && p.LSE != nullptr)
+                p.LSE[size_t(b * p.Hq + h) * N + qrow] = (m[rb] + fast_log2(lt)) * kLn2;
+        }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_qr2_t(FwdParams p, hipStream_t stream) {
+    auto kern = fwd_qr2_kernel<D, CAUSAL>;
+    constexpr size_t lds = qr2_lds_bytes<D>();
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    p.nqb = (p.N + kQr2BM - 1) / kQr2BM;
+    const long long blocks = (long long)p.nqb * p.B * p.Hq;
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kQr2Waves * 64), lds, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(FwdParams p, int d, int causal, hipStream_t stream) {
+    // Only c = scale*log2(e) > 0 reaches the kernel (see the header comment).
+    if (p.scale_log2 > 0.f) {
+        p.qmode = 0;
+    } else if (p.scale_log2 < 0.f) {
+        p.qmode = 1;
+        p.scale_log2 = -p.scale_log2;
+    } else {
+        p.qmode = 2;
+        p.scale_log2 = 1.f;
+    }
     switch (d) {
+#if FA_FWD_PP == 2
+        case 64: return causal ? launch_fwd_qr2_t<64, true>(p, stream) : launch_fwd_qr2_t<64, false>(p, stream);
+        case 128: return causal ? launch_fwd_qr2_t<128, true>(p, stream) : launch_fwd_qr2_t<128, false>(p, stream);
+#elif FA_FWD_PP
+        case 64: return causal ? launch_fwd_pp_t<64, true>(p, stream) : launch_fwd_pp_t<64, false>(p, stream);
+        case 128: return causal ? launch_fwd_pp_t<128, true>(p, stream) : launch_fwd_pp_t<128, false>(p, stream);
+#else
         case 64: return causal ? launch_fwd_bf16_t<64, true>(p, stream) : launch_fwd_bf16_t<64, false>(p, stream);
         case 128: return causal ? launch_fwd_bf16_t<128, true>(p, stream) : launch_fwd_bf16_t<128, false>(p, stream);
+#endif
         case 256: return causal ? launch_fwd_bf16_t<256, true>(p, stream) : launch_fwd_bf16_t<256, false>(p, stream);
         default: return hipErrorInvalidValue;
     }

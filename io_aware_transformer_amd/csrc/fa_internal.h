@@ -17,7 +17,8 @@ struct FwdParams {
     float* LSE;  // may be null
     int B, Hq, Hkv, N;
     float scale_log2;
-    int nqb;  // number of query blocks (filled by the launcher)
+    int nqb;    // number of query blocks (filled by the launcher)
+    int qmode;  // bf16 kernel: 0 use Q, 1 negate Q, 2 zero Q (filled by the launcher)
 };
 
 // Backward launch parameters.
