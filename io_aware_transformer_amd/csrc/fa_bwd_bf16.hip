@@ -29,6 +29,10 @@
 
 #include <math.h>
 
+#ifndef FA_BWD_DKDV_V1
+#define FA_BWD_DKDV_V1 0
+#endif
+
 namespace fa {
 
 size_t bwd_workspace_bytes(int B, int Hq, int N) {
@@ -269,6 +273,262 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------- bwd_dkdv v2
+// One workgroup of 4 waves per (batch, kv head, block of 32*KPW*4 keys); each
+// wave keeps KPW blocks of 32 keys (K and V rows as MFMA B operands) and
+// their dK, dV accumulators.  Query tiles of 64 rows (Q, dO in padded K
+// slabs, LSE and D) are copied global -> LDS by buffer loads, 3-stage, two
+// tiles ahead.  With KPW = 2 every Q / dO fragment read from LDS feeds two
+// products (LDS traffic per FLOP halves); the accumulators are touched by
+// the matrix cores only until the epilogue.
+template <int D>
+struct DkCfg;
+template <>
+struct DkCfg<64> {
+    static constexpr int KPW = 2;
+};
+template <>
+struct DkCfg<128> {
+    static constexpr int KPW = 1;
+};
+constexpr int kDkWaves = 4;
+constexpr int kDkBQ = 64;
+constexpr int kDkStages = 3;
+
+template <int D>
+struct DkLds {
+    using QL = PadSlab<kDkBQ, D>;
+    static constexpr int TILE_BYTES = QL::ELEMS * 2;
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES + 2 * kDkBQ * 4;
+    static constexpr size_t BYTES = size_t(kDkStages) * STAGE_BYTES;
+    static_assert(STAGE_BYTES % 16 == 0, "stage must keep 16-byte alignment");
+};
+
+template <int D>
+constexpr int dk_keys_per_wg() {
+    return 32 * DkCfg<D>::KPW * kDkWaves;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDkWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv2_kernel(BwdParams p) {
+    constexpr int KPW = DkCfg<D>::KPW;
+    using QL = typename DkLds<D>::QL;
+    constexpr int TB = DkLds<D>::TILE_BYTES;
+    constexpr int SB = DkLds<D>::STAGE_BYTES;
+    constexpr int NST = kDkStages;
+    constexpr int BQ = kDkBQ;
+    constexpr int PPW = QL::PIECES / kDkWaves;  // copy pieces per wave per matrix
+    static_assert(QL::PIECES % kDkWaves == 0, "pieces must split over the waves");
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int N = p.N;
+    const float c = p.scale_log2;
+    const int units = p.B * p.Hkv;
+    const int slot = blockIdx.x / units;
+    const int unit = remap_unit(blockIdx.x - slot * units, units);
+    const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
+    const int G = p.Hq / p.Hkv;
+    const int kstart = slot * dk_keys_per_wg<D>();
+    const int kw0 = kstart + 32 * KPW * w;  // first key of this wave (uniform)
+
+    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
+    const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
+
+    bf16x8 kreg[KPW][D / 16], vreg[KPW][D / 16];
+    f32x16 dk[KPW][D / 32], dv[KPW][D / 32];
+#pragma unroll
+    for (int kb = 0; kb < KPW; ++kb) {
+        const int key = kw0 + 32 * kb + l32;
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+            if (key < N) {
+                kreg[kb][cc] = as_bf16x8(ld16(Kh + size_t(key) * D + 16 * cc + 8 * hi));
+                vreg[kb][cc] = as_bf16x8(ld16(Vh + size_t(key) * D + 16 * cc + 8 * hi));
+            } else {
+                kreg[kb][cc] = bf16x8{};
+                vreg[kb][cc] = bf16x8{};
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            dk[kb][db] = f32x16{};
+            dv[kb][db] = f32x16{};
+        }
+    }
+
+    const int nqt = (N + BQ - 1) / BQ;
+    const int qt_first = CAUSAL ? kstart / BQ : 0;
+    const int per_head = nqt - qt_first;
+    const int iters = G * per_head;
+
+    // Per-lane copy sources: piece pi = w + 4 i of the Q (and dO) tile.
+    int src_off[PPW];
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+        int r, e0;
+        QL::piece_src(w + kDkWaves * i, lane, r, e0);
+        src_off[i] = r * D + e0;
+    }
+    auto issue = [&](int t) {
+        const int hq = g * G + t / per_head;
+        const int q0 = (qt_first + t % per_head) * BQ;
+        const size_t row0 = size_t(b * p.Hq + hq) * size_t(N) + q0;
+        unsigned char* st = smem_raw + (t % NST) * SB;
+        const uint32_t bytes = uint32_t(N - q0) * uint32_t(D * 2);
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const bf16*>(p.Q) + row0 * D, bytes);
+        const __amdgpu_buffer_rsrc_t orr = make_rsrc(static_cast<const bf16*>(p.dO) + row0 * D, bytes);
+        const bool tail = q0 + BQ > N;
+#pragma unroll
+        for (int i = 0; i < PPW; ++i) {
+            const int pi = w + kDkWaves * i;
+            uint32_t off = uint32_t(src_off[i]);
+            if (tail) off = uint32_t(min(src_off[i] / D, N - 1 - q0) * D + src_off[i] % D);
+            buf16_to_lds(qr, 2 * off, st + 2 * QL::piece_dst(pi));
+            buf16_to_lds(orr, 2 * off, st + TB + 2 * QL::piece_dst(pi));
+        }
+        // LSE and D of the 64 rows: 256 bytes each, lanes 0..15 of waves 0 / 1.
+        if (w < 2 && lane < 16) {
+            const float* src = (w == 0 ? p.LSE : p.Drow) + row0;
+            const __amdgpu_buffer_rsrc_t rr = make_rsrc(src, uint32_t(N - q0) * 4u);
+            buf16_to_lds(rr, uint32_t(16 * lane), st + 2 * TB + w * BQ * 4);
+        }
+    };
+    // s_waitcnt vmcnt: allow this wave's copies of the newest tile to stay in flight.
+    auto wait_older = [&]() {
+        if (w < 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW + 1) & 15) | (((2 * PPW + 1) >> 4) << 14));
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW) & 15) | (((2 * PPW) >> 4) << 14));
+    };
+
+    const int trow = 4 * hi + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    if (iters > 0) issue(0);
+    if (iters > 1) issue(1);
+    wait_vmem();
+    __syncthreads();
+
+    for (int t = 0; t < iters; ++t) {
+        const bool more = t + 2 < iters;
+        if (more) issue(t + 2);
+        const unsigned char* st = smem_raw + (t % NST) * SB;
+        const bf16* Qs = reinterpret_cast<const bf16*>(st);
+        const bf16* dOs = reinterpret_cast<const bf16*>(st + TB);
+        const float* ls = reinterpret_cast<const float*>(st + 2 * TB);
+        const float* dsr = ls + BQ;
+        const int q0 = (qt_first + t % per_head) * BQ;
+
+#pragma unroll
+        for (int qs = 0; qs < BQ / 32; ++qs) {
+            const int qb0 = q0 + 32 * qs;
+            bool act[KPW];
+#pragma unroll
+            for (int kb = 0; kb < KPW; ++kb) act[kb] = (!CAUSAL || qb0 + 31 >= kw0 + 32 * kb) && qb0 < N;
+            if (!act[0]) continue;  // block 0 has the smallest keys
+            // S = Q K^T, dP = dO V^T: lane = key, register r = query qb0 + 8(r/4) + 4hi + r%4
+            f32x16 sacc[KPW], dpacc[KPW];
+#pragma unroll
+            for (int kb = 0; kb < KPW; ++kb) sacc[kb] = dpacc[kb] = f32x16{};
+#pragma unroll
+            for (int cc = 0; cc < D / 16; ++cc) {
+                const bf16x8 aq = as_bf16x8(ld16(Qs + QL::off(32 * qs + l32, 16 * cc + 8 * hi)));
+                const bf16x8 ao = as_bf16x8(ld16(dOs + QL::off(32 * qs + l32, 16 * cc + 8 * hi)));
+#pragma unroll
+                for (int kb = 0; kb < KPW; ++kb) {
+                    if (!act[kb]) continue;
+                    sacc[kb] = mfma_32x32x16(aq, kreg[kb][cc], sacc[kb]);
+                    dpacc[kb] = mfma_32x32x16(ao, vreg[kb][cc], dpacc[kb]);
+                }
+            }
+            float lq[16], dq[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 lv = *reinterpret_cast<const f32x4*>(ls + 32 * qs + 8 * j + 4 * hi);
+                const f32x4 dv4 = *reinterpret_cast<const f32x4*>(dsr + 32 * qs + 8 * j + 4 * hi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lq[4 * j + e] = lv[e] * kLog2e;
+                    dq[4 * j + e] = dv4[e];
+                }
+            }
+            bf16x8 pb[KPW][2], sb[KPW][2];
+#pragma unroll
+            for (int kb = 0; kb < KPW; ++kb) {
+                float pr[16], ds[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    pr[r] = fast_exp2(fmaf(sacc[kb][r], c, -lq[r]));
+                    ds[r] = pr[r] * (dpacc[kb][r] - dq[r]);
+                }
+                const int key0 = kw0 + 32 * kb;
+                if ((CAUSAL && qb0 < key0 + 31) || qb0 + 31 >= N) {
+                    // hide q < key (causal) and rows q >= N: both P and dS become 0
+                    const int thr = CAUSAL ? key0 + l32 - qb0 - 4 * hi : -1;
+                    const int nlim = N - qb0 - 4 * hi;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qo = 8 * (r >> 2) + (r & 3);
+                        const bool hide = (qo < thr) || (qo >= nlim);
+                        pr[r] = hide ? 0.f : pr[r];
+                        ds[r] = hide ? 0.f : ds[r];
+                    }
+                }
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    pb[kb][cc] = to_bf16x8(pr[8 * cc + 0], pr[8 * cc + 1], pr[8 * cc + 2], pr[8 * cc + 3], pr[8 * cc + 4],
+                                           pr[8 * cc + 5], pr[8 * cc + 6], pr[8 * cc + 7]);
+                    sb[kb][cc] = to_bf16x8(ds[8 * cc + 0], ds[8 * cc + 1], ds[8 * cc + 2], ds[8 * cc + 3], ds[8 * cc + 4],
+                                           ds[8 * cc + 5], ds[8 * cc + 6], ds[8 * cc + 7]);
+                }
+            }
+            // dV += P^T dO, dK += dS^T Q: dO and Q enter as B operands through
+            // transposing reads, each fragment feeding KPW products.
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int qr = 32 * qs + 16 * cc + trow;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const bf16x8 bo = cat(lds_read_tr(dOs + QL::off(qr, db * 32 + tcol)),
+                                          lds_read_tr(dOs + QL::off(qr + 8, db * 32 + tcol)));
+                    const bf16x8 bq = cat(lds_read_tr(Qs + QL::off(qr, db * 32 + tcol)),
+                                          lds_read_tr(Qs + QL::off(qr + 8, db * 32 + tcol)));
+#pragma unroll
+                    for (int kb = 0; kb < KPW; ++kb) {
+                        if (!act[kb]) continue;
+                        dv[kb][db] = mfma_32x32x16(pb[kb][cc], bo, dv[kb][db]);
+                        dk[kb][db] = mfma_32x32x16(sb[kb][cc], bq, dk[kb][db]);
+                    }
+                }
+            }
+        }
+        if (more) wait_older();
+        else wait_vmem();
+        __syncthreads();
+    }
+
+    // Epilogue: lane holds dim db*32 + l32 of keys kw0 + 32kb + 8(r/4) + 4hi + r%4.
+    bf16* dKh = static_cast<bf16*>(p.dK) + kvoff;
+    bf16* dVh = static_cast<bf16*>(p.dV) + kvoff;
+#pragma unroll
+    for (int kb = 0; kb < KPW; ++kb) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = kw0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+                if (kk < N) {
+                    dKh[size_t(kk) * D + db * 32 + l32] = (bf16)(dk[kb][db][r] * p.scale);
+                    dVh[size_t(kk) * D + db * 32 + l32] = (bf16)(dv[kb][db][r]);
+                }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- bwd_dq
 constexpr int kQB = 128;  // query rows per workgroup (32 per wave)
 constexpr int kBNdq = 64;  // keys per staged tile
@@ -424,6 +684,199 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------- bwd_dq v2
+// One workgroup of 4 waves per (batch, query head, 256 queries); each wave
+// owns two 32-row blocks (Q and dO rows as B operands, dQ accumulators), so
+// every K / V fragment read from LDS feeds two products.  K/V tiles of 64
+// keys (padded K slabs: row reads for S^T = K Q^T, transposing reads for
+// dQ^T += K^T dS^T) are copied global -> LDS by buffer loads, 3-stage.
+constexpr int kDqWaves = 4;
+constexpr int kDqBM = 64 * kDqWaves;
+constexpr int kDqBN = 64;
+constexpr int kDqStages = 3;
+
+template <int D>
+struct DqLds {
+    using KL = PadSlab<kDqBN, D>;
+    static constexpr int TILE_BYTES = KL::ELEMS * 2;
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+    static constexpr size_t BYTES = size_t(kDqStages) * STAGE_BYTES;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq2_kernel(BwdParams p) {
+    using KL = typename DqLds<D>::KL;
+    constexpr int TB = DqLds<D>::TILE_BYTES;
+    constexpr int SB = DqLds<D>::STAGE_BYTES;
+    constexpr int NST = kDqStages;
+    constexpr int BN = kDqBN;
+    constexpr int PPW = KL::PIECES / kDqWaves;
+    static_assert(KL::PIECES % kDqWaves == 0, "pieces must split over the waves");
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int N = p.N;
+    const float c = p.scale_log2;
+    const int units = p.B * p.Hq;
+    const int slot = blockIdx.x / units;
+    const int unit = remap_unit(blockIdx.x - slot * units, units);
+    const int qb = CAUSAL ? p.nqb - 1 - slot : slot;
+    const int b = unit / p.Hq, h = unit - (unit / p.Hq) * p.Hq;
+    const int g = h / (p.Hq / p.Hkv);
+    const size_t qrows = size_t(b * p.Hq + h) * size_t(N);
+    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const bf16* __restrict__ Qh = static_cast<const bf16*>(p.Q) + qrows * D;
+    const bf16* __restrict__ dOh = static_cast<const bf16*>(p.dO) + qrows * D;
+    const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
+    const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
+
+    const int q0 = qb * kDqBM;
+    const int wq0 = q0 + 64 * w;
+    const int wq_last = wq0 + 63;
+
+    bf16x8 qreg[2][D / 16], oreg[2][D / 16];
+    float lse2[2], drow[2];
+    int key_lim[2];
+    f32x16 acc[2][D / 32];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int qrow = wq0 + 32 * rb + l32;
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+            if (qrow < N) {
+                qreg[rb][cc] = as_bf16x8(ld16(Qh + size_t(qrow) * D + 16 * cc + 8 * hi));
+                oreg[rb][cc] = as_bf16x8(ld16(dOh + size_t(qrow) * D + 16 * cc + 8 * hi));
+            } else {
+                qreg[rb][cc] = bf16x8{};
+                oreg[rb][cc] = bf16x8{};
+            }
+        }
+        // rows past N: LSE = +inf makes P exactly 0
+        lse2[rb] = (qrow < N) ? p.LSE[qrows + qrow] * kLog2e : INFINITY;
+        drow[rb] = (qrow < N) ? p.Drow[qrows + qrow] : 0.f;
+        key_lim[rb] = CAUSAL ? min(qrow, N - 1) : N - 1;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[rb][db] = f32x16{};
+    }
+
+    const int kend = CAUSAL ? min(N, q0 + kDqBM) : N;
+    const int ntiles = (kend + BN - 1) / BN;
+
+    int src_off[PPW];
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+        int r, e0;
+        KL::piece_src(w + kDqWaves * i, lane, r, e0);
+        src_off[i] = r * D + e0;
+    }
+    auto issue = [&](int kt) {
+        const int key0 = kt * BN;
+        unsigned char* st = smem_raw + (kt % NST) * SB;
+        const uint32_t bytes = uint32_t(N - key0) * uint32_t(D * 2);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kh + size_t(key0) * D, bytes);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vh + size_t(key0) * D, bytes);
+        const bool tail = key0 + BN > N;
+#pragma unroll
+        for (int i = 0; i < PPW; ++i) {
+            const int pi = w + kDqWaves * i;
+            uint32_t off = uint32_t(src_off[i]);
+            if (tail) off = uint32_t(min(src_off[i] / D, N - 1 - key0) * D + src_off[i] % D);
+            buf16_to_lds(kr, 2 * off, st + 2 * KL::piece_dst(pi));
+            buf16_to_lds(vr, 2 * off, st + TB + 2 * KL::piece_dst(pi));
+        }
+    };
+
+    const int trow = 4 * hi + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    if (ntiles > 0) issue(0);
+    if (ntiles > 1) issue(1);
+    wait_vmem();
+    __syncthreads();
+
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const bool more = kt + 2 < ntiles;
+        if (more) issue(kt + 2);
+        const bf16* Ks = reinterpret_cast<const bf16*>(smem_raw + (kt % NST) * SB);
+        const bf16* Vs = reinterpret_cast<const bf16*>(smem_raw + (kt % NST) * SB + TB);
+        const int kstart = kt * BN;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+            const int kb0 = kstart + 32 * kb;
+            if ((CAUSAL && kb0 > wq_last) || kb0 >= N) continue;
+            // S^T = K Q^T, dP^T = V dO^T for both row blocks: lane = query,
+            // register r = key kb0 + 8(r/4) + 4hi + r%4
+            f32x16 s[2], dpt[2];
+            s[0] = s[1] = dpt[0] = dpt[1] = f32x16{};
+#pragma unroll
+            for (int cc = 0; cc < D / 16; ++cc) {
+                const bf16x8 ak = as_bf16x8(ld16(Ks + KL::off(32 * kb + l32, 16 * cc + 8 * hi)));
+                const bf16x8 av = as_bf16x8(ld16(Vs + KL::off(32 * kb + l32, 16 * cc + 8 * hi)));
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    s[rb] = mfma_32x32x16(ak, qreg[rb][cc], s[rb]);
+                    dpt[rb] = mfma_32x32x16(av, oreg[rb][cc], dpt[rb]);
+                }
+            }
+            bf16x8 sb[2][2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                float ds[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pr = fast_exp2(fmaf(s[rb][r], c, -lse2[rb]));
+                    ds[r] = pr * (dpt[rb][r] - drow[rb]);
+                }
+                if ((CAUSAL && kb0 + 31 > wq0 + 32 * rb) || kb0 + 31 >= N) {
+                    const int lim = key_lim[rb] - kb0 - 4 * hi;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) ds[r] = (8 * (r >> 2) + (r & 3) > lim) ? 0.f : ds[r];
+                }
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc)
+                    sb[rb][cc] = to_bf16x8(ds[8 * cc + 0], ds[8 * cc + 1], ds[8 * cc + 2], ds[8 * cc + 3], ds[8 * cc + 4],
+                                           ds[8 * cc + 5], ds[8 * cc + 6], ds[8 * cc + 7]);
+            }
+            // dQ^T += K^T dS^T: K^T through transposing reads, each fragment feeding two products
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int kr = 32 * kb + 16 * cc + trow;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const bf16x8 a = cat(lds_read_tr(Ks + KL::off(kr, db * 32 + tcol)),
+                                         lds_read_tr(Ks + KL::off(kr + 8, db * 32 + tcol)));
+                    acc[0][db] = mfma_32x32x16(a, sb[0][cc], acc[0][db]);
+                    acc[1][db] = mfma_32x32x16(a, sb[1][cc], acc[1][db]);
+                }
+            }
+        }
+        if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW) & 15) | (((2 * PPW) >> 4) << 14));
+        else wait_vmem();
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int qrow = wq0 + 32 * rb + l32;
+        if (qrow < N) {
+            bf16* dQr = static_cast<bf16*>(p.dQ) + qrows * D + size_t(qrow) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x4 v =
+                        bf16x4{(bf16)(acc[rb][db][4 * j + 0] * p.scale), (bf16)(acc[rb][db][4 * j + 1] * p.scale),
+                               (bf16)(acc[rb][db][4 * j + 2] * p.scale), (bf16)(acc[rb][db][4 * j + 3] * p.scale)};
+                    *reinterpret_cast<bf16x4*>(dQr + db * 32 + 8 * j + 4 * hi) = v;
+                }
+            }
+        }
+    }
+}
+
 template <typename K>
 hipError_t set_lds(K kern, size_t bytes, bool& done) {
     if (done) return hipSuccess;
@@ -444,6 +897,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     if (e != hipSuccess) return e;
 
     // 2. dK, dV
+#if FA_BWD_DKDV_V1
     {
         auto kern = bwd_dkdv_kernel<D, CAUSAL>;
         constexpr size_t lds = 2 * dkdv_stage_bytes<D>();
@@ -454,7 +908,20 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), lds, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+#else
+    {
+        auto kern = bwd_dkdv2_kernel<D, CAUSAL>;
+        constexpr size_t lds = DkLds<D>::BYTES;
+        static bool attr = false;
+        if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
+        p.nkb = (p.N + dk_keys_per_wg<D>() - 1) / dk_keys_per_wg<D>();
+        const long long blocks = (long long)p.nkb * p.B * p.Hkv;
+        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+#endif
     // 3. dQ
+#if FA_BWD_DKDV_V1
     {
         auto kern = bwd_dq_kernel<D, CAUSAL>;
         constexpr size_t lds = size_t(2) * 2 * kBNdq * D * sizeof(bf16);
@@ -465,6 +932,18 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), lds, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+#else
+    {
+        auto kern = bwd_dq2_kernel<D, CAUSAL>;
+        constexpr size_t lds = DqLds<D>::BYTES;
+        static bool attr = false;
+        if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
+        p.nqb = (p.N + kDqBM - 1) / kDqBM;
+        const long long blocks = (long long)p.nqb * p.B * p.Hq;
+        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDqWaves * 64), lds, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+#endif
     return hipSuccess;
 }
 

@@ -141,6 +141,51 @@ __device__ __forceinline__ void vslab_slot(int s, int& r, int& e0) {
     r = rem >> 2;
     e0 = 32 * db + 8 * (rem & 3);
 }
+// Padded K slabs: K slabs with a 128-byte gap after every slab.  Serves both
+// 16-byte row reads (MFMA A operands) and transposing reads (B operands of
+// the transposed product) without bank conflicts: the gap puts the two
+// 16-dim slabs touched by one transposing read in different bank halves.
+template <int ROWS, int D>
+struct PadSlab {
+    static constexpr int SLAB = ROWS * 16 + 64;   // elements per slab incl. gap
+    static constexpr int ELEMS = (D / 16) * SLAB;  // elements per tile
+    static constexpr int PIECES_PER_SLAB = ROWS / 32;  // 1 KB copy pieces
+    static constexpr int PIECES = (D / 16) * PIECES_PER_SLAB;
+    static __device__ __forceinline__ int off(int r, int e) {
+        return (e >> 4) * SLAB + r * 16 + 8 * (((e >> 3) & 1) ^ ((r >> 3) & 1)) + (e & 7);
+    }
+    // LDS element offset of the start of copy piece p.
+    static __device__ __forceinline__ int piece_dst(int p) {
+        return (p / PIECES_PER_SLAB) * SLAB + (p % PIECES_PER_SLAB) * 512;
+    }
+    // Source (row, first element) of the 16 bytes lane l of piece p copies.
+    static __device__ __forceinline__ void piece_src(int p, int l, int& r, int& e0) {
+        const int slab = p / PIECES_PER_SLAB, s = (p % PIECES_PER_SLAB) * 64 + l;
+        r = s >> 1;
+        e0 = 16 * slab + 8 * ((s & 1) ^ ((r >> 3) & 1));
+    }
+};
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer, gfx9 descriptor
+// word 3 = 0x00020000).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16-byte buffer load straight into LDS: lane l writes dst_uniform + 16 l.
+__device__ __forceinline__ void buf16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* dst_uniform) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst_uniform, 16, voff, 0, 0, 0);
+#pragma clang diagnostic pop
+}
+// Wait for this wave's outstanding vector-memory loads (including
+// direct-to-LDS copies): s_waitcnt vmcnt(0), other counters at maximum.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait for this wave's outstanding LDS operations: s_waitcnt lgkmcnt(0).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Element offset of (row r, element e) in a row-read tile.
 template <int D>
 __device__ __forceinline__ int off_row(int r, int e) {

@@ -100,25 +100,6 @@ __device__ __forceinline__ void fwd_decompose(int id, int units, int nqb, int Hq
     h = unit - b * Hq;
 }
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// Buffer resource over `bytes` bytes at `base` (raw buffer, gfx9 descriptor
-// word 3 = 0x00020000).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-// 16-byte buffer load straight into LDS: lane l writes dst_uniform + 16 l.
-__device__ __forceinline__ void buf16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, bf16* dst_uniform) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wold-style-cast"
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst_uniform, 16, voff, 0, 0, 0);
-#pragma clang diagnostic pop
-}
-
-// Wait for this wave's outstanding global loads (including direct-to-LDS
-// copies): s_waitcnt vmcnt(0) with expcnt/lgkmcnt left at their maximum.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 // K/V tiles are copied global -> LDS by the direct-to-LDS load path (no
 // VGPR staging) in 1 KB pieces, one per wave instruction: lane l of piece p
 // writes 16-byte slot 64p + l and fetches the chunk that the tile's slab
@@ -505,7 +486,7 @@ void fwd_pp_kernel(FwdParams p) {
     };
     auto finish = [&](int step) {
         if ((step & 1) && step >= 5) wait_vmem();
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+        wait_lds();  // this wave's LDS writes are done
         __builtin_amdgcn_s_barrier();
     };
     // ---- M phase j: PV of tile j-1, then QK of tile j.  LDS fragments are
