@@ -45,6 +45,35 @@ def alg_bytes_fwd(p):
     return (2 * p.B * p.Hq * p.N * p.d + 2 * p.B * p.Hkv * p.N * p.d) * e + 4 * p.B * p.Hq * p.N
 
 
+FWD_SOURCES = ["io_aware_transformer_amd/csrc/fa_fwd_bf16.hip", "io_aware_transformer_amd/csrc/fa_device.hpp"]
+
+
+def fwd_source_hash():
+    """sha256 over the forward kernel's sources: ties stored counter data to
+    the kernel it was measured on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in FWD_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(p):
+    """HBM bytes per forward launch from profiles/fwd_traffic_<preset>.json
+    (FETCH_SIZE / WRITE_SIZE counter runs scaled by the copy calibration),
+    or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"fwd_traffic_{p.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != fwd_source_hash():
+        return None
+    return t
+
+
 def cpu_baseline(p, passes, budget_s):
     """Time the fp64 oracle on host cores over (b, h) units of the same
     workload until ``budget_s`` of CPU work is done (at least one unit)."""
@@ -95,9 +124,14 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters, then exit")
     ap.add_argument("--traffic-json", default=None,
                     help="JSON file with measured HBM bytes per forward launch ({'fetch_bytes': F, "
-                         "'write_bytes': W}) to report as roofline.traffic")
+                         "'write_bytes': W}) to report as roofline.traffic (default: "
+                         "profiles/fwd_traffic_<preset>.json when it matches the kernel sources)")
+    ap.add_argument("--print-source-hash", action="store_true", help="print the forward sources' sha256 and exit")
     args = ap.parse_args()
 
+    if args.print_source_hash:
+        print(fwd_source_hash())
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU "
               f"path; the per-GPU shard is the single-GPU workload.", file=sys.stderr)
@@ -210,12 +244,17 @@ def main():
             "avg_call_ms": round(bwd_avg, 5),
             "flop_convention": "2.5 x forward",
         }
+    t = None
     if args.traffic_json:
         with open(args.traffic_json) as f:
             t = json.load(f)
+    elif p.dtype == "bf16":
+        t = stored_traffic(p)
+    if t is not None:
         roofline["traffic"] = {"fetch_bytes": t["fetch_bytes"], "write_bytes": t["write_bytes"],
                                "total_bytes": t["fetch_bytes"] + t["write_bytes"],
-                               "alg_bytes": alg_bytes_fwd(p), "source": t.get("source", "")}
+                               "alg_bytes": alg_bytes_fwd(p), "fetch_factor": t.get("fetch_factor"),
+                               "write_factor": t.get("write_factor"), "source": t.get("source", "")}
     line = {
         "metric": "attention fwd/bwd TFLOP/s (bf16, causal, d=128, N=2K-8K) + % MFMA peak",
         "value": round(value, 2),
