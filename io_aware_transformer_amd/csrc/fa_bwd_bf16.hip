@@ -11,10 +11,11 @@
 //
 // Three kernels on the caller's stream:
 //   1. bwd_pre:  D_i = dO_i . O_i (fp32, into the workspace).
-//   2. bwd_dkdv: one workgroup per (batch, kv head, 128 keys); each wave
-//      keeps its 32 keys' K and V rows in registers and its dK, dV
+//   2. bwd_dkdv: one workgroup per (batch, kv head, block of keys); each
+//      wave keeps its keys' K and V rows in registers and its dK, dV
 //      accumulators in registers, and walks every query tile (of every
-//      query head of the group) that can see its keys.  S = Q K^T and
+//      query head of the group) that can see its keys (v2: two 32-key
+//      blocks per wave at d = 64; v3: software-pipelined, d = 128).  S = Q K^T and
 //      dP = dO V^T come out with one key per lane, which is exactly the MFMA
 //      A layout of P^T and dS^T, so dV += P^T dO and dK += dS^T Q take the
 //      score registers directly; dO and Q enter as B operands through
@@ -29,8 +30,16 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #ifndef FA_BWD_DKDV_V1
 #define FA_BWD_DKDV_V1 0
+#endif
+#ifndef FA_BWD_DKDV3
+#define FA_BWD_DKDV3 1
+#endif
+#ifndef FA_BWD_DKDV3_D64
+#define FA_BWD_DKDV3_D64 0
 #endif
 
 namespace fa {
@@ -287,9 +296,12 @@ template <>
 struct DkCfg<64> {
     static constexpr int KPW = 2;
 };
+#ifndef FA_BWD_KPW128
+#define FA_BWD_KPW128 1
+#endif
 template <>
 struct DkCfg<128> {
-    static constexpr int KPW = 1;
+    static constexpr int KPW = FA_BWD_KPW128;
 };
 constexpr int kDkWaves = 4;
 constexpr int kDkBQ = 64;
@@ -524,6 +536,305 @@ void bwd_dkdv2_kernel(BwdParams p) {
                     dKh[size_t(kk) * D + db * 32 + l32] = (bf16)(dk[kb][db][r] * p.scale);
                     dVh[size_t(kk) * D + db * 32 + l32] = (bf16)(dv[kb][db][r]);
                 }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bwd_dkdv v3
+// Software-pipelined key-major dK / dV, one wave per SIMD, 32 keys per wave,
+// query subtiles of 32 rows (two per staged 64-row tile).  Subtile i passes
+// through three steps: A(i) S = Q K^T, dP = dO V^T (matrix cores, row reads
+// of Q / dO issued one step ahead); B(i) P = exp2(c S - LSE log2 e),
+// dS = P o (dP - D) (vector ALU); C(i) dV += P^T dO, dK += dS^T Q (matrix
+// cores, transposing reads of dO / Q).  The loop body for subtile i runs
+// A(i+1) together with B(i) and the transposing reads of C(i), then C(i)
+// together with the row reads for A(i+2): every LDS read has a whole step
+// of slack before its first use, and the LDS traffic is split evenly over
+// the two steps.  (Vector ALU work of a wave overlaps that wave's own
+// matrix-core work only partly on this chip; the gain is the hidden LDS
+// latency.)  Four stages of 64-row tiles; tile t+3 is issued right after
+// the barrier that publishes tile t+1.  Used for d = 128.
+constexpr int kDk3Stages = 4;
+
+template <int D>
+struct Dk3Lds {
+    using QL = PadSlab<kDkBQ, D>;
+    static constexpr int TILE_BYTES = QL::ELEMS * 2;
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES + 2 * kDkBQ * 4;
+    static constexpr size_t BYTES = size_t(kDk3Stages) * STAGE_BYTES;
+    static_assert(STAGE_BYTES % 16 == 0, "stage must keep 16-byte alignment");
+};
+constexpr int kDk3KeysPerWg = 32 * kDkWaves;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDkWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv3_kernel(BwdParams p) {
+    using QL = typename Dk3Lds<D>::QL;
+    constexpr int TB = Dk3Lds<D>::TILE_BYTES;
+    constexpr int SB = Dk3Lds<D>::STAGE_BYTES;
+    constexpr int NST = kDk3Stages;
+    constexpr int BQ = kDkBQ;
+    constexpr int NC = D / 16;   // contraction steps of S and dP
+    constexpr int NDB = D / 32;  // 32-dim blocks of dK and dV
+    constexpr int PPW = QL::PIECES / kDkWaves;
+    static_assert(QL::PIECES % kDkWaves == 0, "pieces must split over the waves");
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int N = p.N;
+    const float c = p.scale_log2;
+    const int units = p.B * p.Hkv;
+    const int slot = blockIdx.x / units;
+    const int unit = remap_unit(blockIdx.x - slot * units, units);
+    const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
+    const int G = p.Hq / p.Hkv;
+    const int kstart = slot * kDk3KeysPerWg;
+    const int kw0 = kstart + 32 * w;  // first key of this wave (uniform)
+
+    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
+    const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
+
+    bf16x8 kreg[NC], vreg[NC];
+    f32x16 dk[NDB], dv[NDB];
+    {
+        const int key = kw0 + l32;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            if (key < N) {
+                kreg[cc] = as_bf16x8(ld16(Kh + size_t(key) * D + 16 * cc + 8 * hi));
+                vreg[cc] = as_bf16x8(ld16(Vh + size_t(key) * D + 16 * cc + 8 * hi));
+            } else {
+                kreg[cc] = bf16x8{};
+                vreg[cc] = bf16x8{};
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
+    }
+
+    const int nqt = (N + BQ - 1) / BQ;
+    const int qt_first = CAUSAL ? kstart / BQ : 0;
+    const int per_head = nqt - qt_first;
+    const int iters = G * per_head;  // >= 1
+
+    int src_off[PPW];
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+        int r, e0;
+        QL::piece_src(w + kDkWaves * i, lane, r, e0);
+        src_off[i] = r * D + e0;
+    }
+    auto tile_q0 = [&](int t) { return (qt_first + t % per_head) * BQ; };
+    // Copy of tile t into its stage by this wave, in 2 PPW + 1 pieces: piece
+    // k < PPW is a 1 KB piece of Q, k < 2 PPW of dO, and piece 2 PPW the
+    // tile's LSE and D (waves 0 and 1, 16 lanes).
+    struct TileCopy {
+        __amdgpu_buffer_rsrc_t q, o, stat;
+        unsigned char* st;
+        int last_row;  // rows past N read row N-1 (their results are hidden)
+    };
+    auto tile_copy = [&](int t) {
+        const int hq = g * G + t / per_head;
+        const int q0 = tile_q0(t);
+        const size_t row0 = size_t(b * p.Hq + hq) * size_t(N) + q0;
+        const uint32_t bytes = uint32_t(N - q0) * uint32_t(D * 2);
+        TileCopy tc;
+        tc.q = make_rsrc(static_cast<const bf16*>(p.Q) + row0 * D, bytes);
+        tc.o = make_rsrc(static_cast<const bf16*>(p.dO) + row0 * D, bytes);
+        tc.stat = make_rsrc((w == 0 ? p.LSE : p.Drow) + row0, uint32_t(N - q0) * 4u);
+        tc.st = smem_raw + (t % NST) * SB;
+        tc.last_row = N - 1 - q0;
+        return tc;
+    };
+    auto copy_piece = [&](const TileCopy& tc, int k) {
+        if (k < 2 * PPW) {
+            const int i = k % PPW, pi = w + kDkWaves * i;
+            const int r = src_off[i] / D;
+            const uint32_t off = uint32_t(r <= tc.last_row ? src_off[i] : tc.last_row * D + src_off[i] % D);
+            if (k < PPW) buf16_to_lds(tc.q, 2 * off, tc.st + 2 * QL::piece_dst(pi));
+            else buf16_to_lds(tc.o, 2 * off, tc.st + TB + 2 * QL::piece_dst(pi));
+        } else if (w < 2 && lane < 16) {
+            buf16_to_lds(tc.stat, uint32_t(16 * lane), tc.st + 2 * TB + w * BQ * 4);
+        }
+    };
+    auto issue = [&](int t) {
+        const TileCopy tc = tile_copy(t);
+#pragma unroll
+        for (int k = 0; k <= 2 * PPW; ++k) copy_piece(tc, k);
+    };
+    // s_waitcnt vmcnt(n): n = this wave's copies of one tile (the newest tile stays in flight).
+    auto wait_all_but_one_tile = [&]() {
+        if (w < 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW + 1) & 15) | (((2 * PPW + 1) >> 4) << 14));
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW) & 15) | (((2 * PPW) >> 4) << 14));
+    };
+
+    const int trow = 4 * hi + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    // Pipeline registers.  Every LDS read has one full step of slack: the
+    // row fragments of A(i+2) are read during C(i), the transposed
+    // fragments of C(i) and nothing else during A(i+1).
+    bf16x8 aq[NC], ao[NC];          // row fragments of Q, dO: A operands of S, dP
+    f32x4 lq4[4], dd4[4];           // LSE and D of the next B step's rows, in groups of 4
+    f32x16 s0, dp0, s1, dp1;        // S, dP of two consecutive subtiles
+    bf16x8 bo[2][NDB], bq[2][NDB];  // transposed dO, Q fragments of the current C step
+    bf16x8 pb[2], sb[2];            // P^T, dS^T of the current subtile
+    float pr[16], ds[16];
+
+    auto stage = [&](int i) -> const unsigned char* { return smem_raw + ((i >> 1) % NST) * SB; };
+    auto load_a = [&](int i, int cc) {
+        const unsigned char* st = stage(i);
+        const bf16* Qs = reinterpret_cast<const bf16*>(st) + 512 * (i & 1);
+        const bf16* dOs = reinterpret_cast<const bf16*>(st + TB) + 512 * (i & 1);
+        aq[cc] = as_bf16x8(lds16(Qs + QL::off(l32, 16 * cc + 8 * hi)));
+        ao[cc] = as_bf16x8(lds16(dOs + QL::off(l32, 16 * cc + 8 * hi)));
+    };
+    auto load_stats = [&](int i, int j) {
+        const float* ls = reinterpret_cast<const float*>(stage(i) + 2 * TB) + 32 * (i & 1);
+        lq4[j] = lds_f32x4(ls + 8 * j + 4 * hi);
+        dd4[j] = lds_f32x4(ls + BQ + 8 * j + 4 * hi);
+    };
+    // Transposing read number n (0 .. 8 NDB - 1) of subtile i's C step.
+    auto load_tr = [&](int i, int n) {
+        const unsigned char* st = stage(i);
+        const int half = n & 1, which = (n >> 1) & 1, db = (n >> 2) % NDB, cc = (n >> 2) / NDB;
+        const bf16* base = reinterpret_cast<const bf16*>(which ? st : st + TB);
+        const int qr = 32 * (i & 1) + 16 * cc + trow + 8 * half;
+        const bf16x4 v = lds_read_tr(base + QL::off(qr, db * 32 + tcol));
+        bf16x8& dst = which ? bq[cc][db] : bo[cc][db];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * half + e] = v[e];
+    };
+    auto needs_mask = [&](int i) {
+        const int qb0 = tile_q0(i >> 1) + 32 * (i & 1);
+        return (CAUSAL && qb0 < kw0 + 31) || qb0 + 31 >= N;
+    };
+    constexpr int RPC = 16 / NC;       // score rows (registers) of B per slot
+    constexpr int TPC = 8 * NDB / NC;  // transposing reads per slot
+    static_assert(RPC * NC == 16 && TPC * NC == 8 * NDB && 2 * NDB == NC, "slots must divide the work");
+
+    // Step 1 of subtile i, NC slots of two MFMAs: A(i+1), with B(i) (RPC
+    // rows per slot) and the transposing reads of C(i).  Scheduling fences
+    // keep the slots in order; the order inside a slot is the compiler's.
+    auto step1 = [&](int i, const f32x16& s_cur, const f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt,
+                     bool has_next, auto masked) {
+        const int qb0 = tile_q0(i >> 1) + 32 * (i & 1);
+        const int thr = CAUSAL ? kw0 + l32 - qb0 - 4 * hi : -1 - 4 * hi;
+        const int nlim = N - qb0 - 4 * hi;
+        if (has_next) s_nxt = dp_nxt = f32x16{};
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            if (has_next) {
+                s_nxt = mfma_32x32x16(aq[k], kreg[k], s_nxt);
+                dp_nxt = mfma_32x32x16(ao[k], vreg[k], dp_nxt);
+            }
+#pragma unroll
+            for (int n = k * TPC; n < (k + 1) * TPC; ++n) load_tr(i, n);
+#pragma unroll
+            for (int r = k * RPC; r < (k + 1) * RPC; ++r) {
+                float ex = fmaf(s_cur[r], c, -lq4[r >> 2][r & 3] * kLog2e);
+                if constexpr (decltype(masked)::value) {
+                    const int qo = 8 * (r >> 2) + (r & 3);
+                    ex = (qo < thr || qo >= nlim) ? -INFINITY : ex;
+                }
+                pr[r] = fast_exp2(ex);
+                ds[r] = pr[r] * (dp_cur[r] - dd4[r >> 2][r & 3]);
+                if ((r & 7) == 7) {
+                    const int cc = r >> 3;
+                    pb[cc] = to_bf16x8(pr[8 * cc + 0], pr[8 * cc + 1], pr[8 * cc + 2], pr[8 * cc + 3],
+                                       pr[8 * cc + 4], pr[8 * cc + 5], pr[8 * cc + 6], pr[8 * cc + 7]);
+                    sb[cc] = to_bf16x8(ds[8 * cc + 0], ds[8 * cc + 1], ds[8 * cc + 2], ds[8 * cc + 3],
+                                       ds[8 * cc + 4], ds[8 * cc + 5], ds[8 * cc + 6], ds[8 * cc + 7]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Step 2 of subtile i, NC slots of two MFMAs: C(i), with the row reads of
+    // A(i+2) and the statistics of subtile i+1.
+    // Optionally also spreads the copy of a tile over the slots (one piece
+    // per slot instead of a burst that queues in the address unit).
+    auto step2 = [&](int i, bool has_next, bool has_next2) {
+#pragma unroll
+        for (int m = 0; m < NC; ++m) {
+            const int cc = m / NDB, db = m % NDB;
+            dv[db] = mfma_32x32x16(pb[cc], bo[cc][db], dv[db]);
+            dk[db] = mfma_32x32x16(sb[cc], bq[cc][db], dk[db]);
+            if (has_next2) load_a(i + 2, m);
+            if (has_next && m < 4) load_stats(i + 1, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto body = [&](int i, const f32x16& s_cur, const f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt, bool has_next,
+                    bool has_next2) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (needs_mask(i)) step1(i, s_cur, dp_cur, s_nxt, dp_nxt, has_next, std::true_type{});
+        else step1(i, s_cur, dp_cur, s_nxt, dp_nxt, has_next, std::false_type{});
+        if ((i & 1) == 0) {
+            // Publish tile t+1: this wave's copies of it are done once only
+            // tile t+2's remain in flight.  Tile t-1 was last read (and
+            // waited for) in the previous body, so its stage is refilled
+            // with tile t+3 right after the barrier.
+            const int t = i >> 1;
+            if (t + 2 < iters) wait_all_but_one_tile();
+            else wait_vmem();
+            __builtin_amdgcn_s_barrier();
+            // One burst per wave: the address unit takes ~16 cycles per 1 KB
+            // piece whichever way the pieces are spread over the step.
+            if (t + 3 < iters) issue(t + 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        step2(i, has_next, has_next2);
+    };
+
+    issue(0);
+    if (iters > 1) issue(1);
+    if (iters > 2) issue(2);
+    if (iters > 2) {
+        if (w < 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * PPW + 2) & 15) | (((4 * PPW + 2) >> 4) << 14));
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * PPW) & 15) | (((4 * PPW) >> 4) << 14));
+    } else if (iters > 1) {
+        wait_all_but_one_tile();
+    } else {
+        wait_vmem();
+    }
+    __builtin_amdgcn_s_barrier();
+    // A(0) outright, then the row reads of A(1) and the statistics of subtile 0.
+    s0 = dp0 = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+        load_a(0, cc);
+        s0 = mfma_32x32x16(aq[cc], kreg[cc], s0);
+        dp0 = mfma_32x32x16(ao[cc], vreg[cc], dp0);
+    }
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) load_a(1, cc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_stats(0, j);
+
+    const int nsub = 2 * iters;
+    for (int i = 0; i + 2 < nsub; i += 2) {
+        body(i, s0, dp0, s1, dp1, true, true);
+        body(i + 1, s1, dp1, s0, dp0, true, true);
+    }
+    body(nsub - 2, s0, dp0, s1, dp1, true, false);
+    body(nsub - 1, s1, dp1, s0, dp0, false, false);
+    wait_vmem();  // no copy into LDS may outlive the workgroup
+
+    bf16* dKh = static_cast<bf16*>(p.dK) + kvoff;
+    bf16* dVh = static_cast<bf16*>(p.dV) + kvoff;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (kk < N) {
+                dKh[size_t(kk) * D + db * 32 + l32] = (bf16)(dk[db][r] * p.scale);
+                dVh[size_t(kk) * D + db * 32 + l32] = (bf16)(dv[db][r]);
             }
         }
     }
@@ -909,7 +1220,16 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 #else
-    {
+    if (FA_BWD_DKDV3 && (D == 128 || FA_BWD_DKDV3_D64)) {
+        auto kern = bwd_dkdv3_kernel<D, CAUSAL>;
+        constexpr size_t lds = Dk3Lds<D>::BYTES;
+        static bool attr = false;
+        if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
+        p.nkb = (p.N + kDk3KeysPerWg - 1) / kDk3KeysPerWg;
+        const long long blocks = (long long)p.nkb * p.B * p.Hkv;
+        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
         auto kern = bwd_dkdv2_kernel<D, CAUSAL>;
         constexpr size_t lds = DkLds<D>::BYTES;
         static bool attr = false;

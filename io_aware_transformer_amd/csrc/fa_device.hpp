@@ -39,8 +39,19 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// LDS reads of data that arrives by direct buffer-to-LDS copies.  The
+// restrict-qualified pointer gives each read scoped alias information; the
+// compiler then leaves the wait for those copies (s_waitcnt vmcnt) to the
+// kernel, which waits for its own copies explicitly before the barrier that
+// publishes a tile, instead of waiting for every copy in flight (including
+// prefetches of later tiles) before the first LDS read.
+__device__ __forceinline__ u32x4 lds16(const void* __restrict__ p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ f32x4 lds_f32x4(const float* __restrict__ p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+
 // Transposing 8-byte LDS read (see the layout note at the top).
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* __restrict__ p) {
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wold-style-cast"
@@ -185,6 +196,16 @@ __device__ __forceinline__ void buf16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Wait for this wave's outstanding LDS operations: s_waitcnt lgkmcnt(0).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier for kernels whose LDS tiles arrive by direct
+// buffer-to-LDS copies.  Every wave has already waited for its own copies
+// of the tile being published (s_waitcnt vmcnt); draining this wave's LDS
+// reads first keeps a later copy into a reused stage from overtaking them.
+// Unlike __syncthreads(), whose fence also waits for every copy still in
+// flight (the prefetches of later tiles), this waits for nothing else.
+__device__ __forceinline__ void barrier_lds() {
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+}
 
 // Element offset of (row r, element e) in a row-read tile.
 template <int D>
