@@ -8,9 +8,11 @@ and imports nothing from it.
 
 The oracle is the plain definition of attention (materialise the score
 matrix, stable row softmax, multiply by V) and the textbook analytic
-backward, in float64, one (batch, query-head) unit at a time.  Every
+backward, in float64, one (batch, query-head) unit at a time, plus
+attention with queries and keys of different lengths, attention over a key
+range, and the merge of partial results over disjoint key ranges.  Every
 function cites the passage of the source pages it follows; see
-``oracle/attention.py``.
+``oracle/attention.py`` and ``oracle/splitkv.py``.
 """
 
 from .attention import (
@@ -21,6 +23,7 @@ from .attention import (
     head_backward,
     kv_head_of,
 )
+from .splitkv import cross_forward, merge_partials, partial_forward
 
 __all__ = [
     "attention_forward",
@@ -29,4 +32,7 @@ __all__ = [
     "head_forward",
     "head_backward",
     "kv_head_of",
+    "cross_forward",
+    "partial_forward",
+    "merge_partials",
 ]

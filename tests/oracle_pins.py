@@ -6,8 +6,9 @@ as written; ``test_oracle_mutants.py`` runs them against deliberately broken
 copies of the oracle's internals (a dropped scale, a wrong mask, a missing
 term, a transposed operand ...) and requires each break to be caught.
 
-The checks look the oracle up through the ``oracle.attention`` module at call
-time, so a patched module attribute is what they exercise.
+The checks look the oracle up through the ``oracle.attention`` and
+``oracle.splitkv`` modules at call time, so a patched module attribute is
+what they exercise.
 """
 
 import math
@@ -16,6 +17,7 @@ import os
 import numpy as np
 
 import oracle.attention as OA
+import oracle.splitkv as OS
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -325,6 +327,103 @@ def check_forward_rows(seed=16):
         assert abs(LSEr[t] - math.log(i + 1)) < 1e-14
 
 
+# ---------------------------------------------------------------- split keys
+
+
+def _qkv(rng, B, Hq, Hkv, n_q, n_k, d):
+    return (rng.standard_normal((B, Hq, n_q, d)), rng.standard_normal((B, Hkv, n_k, d)),
+            rng.standard_normal((B, Hkv, n_k, d)))
+
+
+def check_cross_square(seed=17):
+    """N_q = N_k reproduces the square definition of oracle.attention."""
+    rng = np.random.default_rng(seed)
+    Q, K, V = _qkv(rng, 2, 4, 2, 11, 11, 8)
+    for causal in (False, True):
+        O, LSE = OS.cross_forward(Q, K, V, 0.3, causal)
+        Or, LSEr = OA.attention_forward(Q, K, V, 0.3, causal)
+        assert np.max(np.abs(O - Or)) < 1e-14 and np.max(np.abs(LSE - LSEr)) < 1e-13
+
+
+def check_cross_suffix(seed=18):
+    """Bottom-right causal alignment: N_q queries against N_k keys are the last
+    N_q rows of the square problem whose queries extend them to N_k rows."""
+    rng = np.random.default_rng(seed)
+    n_k, d = 13, 6
+    Qf, K, V = _qkv(rng, 1, 2, 1, n_k, n_k, d)
+    Of, LSEf = OA.attention_forward(Qf, K, V, 0.45, True)
+    for n_q in (1, 2, 5, n_k):
+        O, LSE = OS.cross_forward(Qf[:, :, n_k - n_q:], K, V, 0.45, True)
+        assert np.max(np.abs(O - Of[:, :, n_k - n_q:])) < 1e-14
+        assert np.max(np.abs(LSE - LSEf[:, :, n_k - n_q:])) < 1e-13
+    # one query (decoding) sees every key: causal equals non-causal
+    O1, L1 = OS.cross_forward(Qf[:, :, :1], K, V, 0.45, True)
+    O0, L0 = OS.cross_forward(Qf[:, :, :1], K, V, 0.45, False)
+    assert np.max(np.abs(O1 - O0)) < 1e-15 and np.max(np.abs(L1 - L0)) < 1e-15
+    # more queries than keys: the first N_q - N_k rows see nothing
+    Q2, K2, V2 = _qkv(rng, 1, 1, 1, 7, 4, 3)
+    O2, L2 = OS.cross_forward(Q2, K2, V2, 1.0, True)
+    assert np.all(O2[0, 0, :3] == 0) and np.all(L2[0, 0, :3] == -np.inf)
+    O2s, L2s = OA.attention_forward(Q2[:, :, 3:], K2, V2, 1.0, True)
+    assert np.max(np.abs(O2[:, :, 3:] - O2s)) < 1e-14 and np.max(np.abs(L2[:, :, 3:] - L2s)) < 1e-13
+
+
+def check_merge_four_token():
+    """The printed example merged from its two key tiles: row A's tile (A, B)
+    holds scores {1, 2}, tile (C, D) holds {3, 4}; merged LSE = 4 + ln
+    1.5530018 and the merged weights are the softmax of [1, 2, 3, 4]."""
+    s = load_four_token_example()["scores"]
+    eye = np.eye(4)
+    Q, K, V = s[None, None], eye[None, None], eye[None, None]
+    parts = [OS.partial_forward(Q, K, V, 1.0, False, 0, 2), OS.partial_forward(Q, K, V, 1.0, False, 2, 4)]
+    assert abs(parts[0][1][0, 0, 0] - (2 + math.log(L_TILE))) < 1e-7
+    assert abs(parts[1][1][0, 0, 0] - (4 + math.log(L_TILE))) < 1e-7
+    O, LSE = OS.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    for i in range(4):
+        want = np.array([SOFTMAX_1234[x] for x in s[i]])
+        assert np.max(np.abs(O[0, 0, i] - want)) < 1e-7
+        assert abs(LSE[0, 0, i] - LSE_1234) < 1e-7
+
+
+def check_merge_partition(seed=19):
+    """Merging the partial results of any partition of the keys (empty blocks
+    included) gives attention over all keys, causal or not, N_q <> N_k."""
+    rng = np.random.default_rng(seed)
+    for n_q, n_k in ((1, 37), (5, 37), (37, 37), (9, 4)):
+        Q, K, V = _qkv(rng, 2, 4, 2, n_q, n_k, 5)
+        for causal in (False, True):
+            want_o, want_l = OS.cross_forward(Q, K, V, 0.7, causal)
+            for cuts in ([0, n_k], [0, 0, n_k], [0, 1, n_k // 2, n_k], list(range(0, n_k + 1, 3)) + [n_k]):
+                cuts = sorted(set(min(c, n_k) for c in cuts))
+                parts = [OS.partial_forward(Q, K, V, 0.7, causal, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+                parts.append(OS.partial_forward(Q, K, V, 0.7, causal, n_k, n_k))  # an empty block
+                O, LSE = OS.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+                live = np.isfinite(want_l)
+                assert np.array_equal(np.isfinite(LSE), live)
+                assert np.max(np.abs(O - want_o)) < 1e-13
+                assert np.max(np.abs(LSE[live] - want_l[live])) < 1e-12
+
+
+def check_merge_properties(seed=20):
+    """One part is returned unchanged; order does not matter; all-empty rows
+    stay (0, -inf); values far from 1 do not overflow."""
+    rng = np.random.default_rng(seed)
+    Op = rng.standard_normal((3, 4, 6))
+    Lp = rng.standard_normal((3, 4)) * 50.0
+    O1, L1 = OS.merge_partials(Op[:1], Lp[:1])
+    assert np.max(np.abs(O1 - Op[0])) < 1e-15 and np.max(np.abs(L1 - Lp[0])) < 1e-15
+    Oa, La = OS.merge_partials(Op, Lp)
+    Ob, Lb = OS.merge_partials(Op[::-1], Lp[::-1])
+    assert np.max(np.abs(Oa - Ob)) < 1e-14 and np.max(np.abs(La - Lb)) < 1e-12
+    # closed form for two parts with LSE a, b: weights e^a / (e^a + e^b)
+    a, b = 700.0, 699.0
+    O2, L2 = OS.merge_partials(np.array([[[1.0]], [[0.0]]]), np.array([[a], [b]]))
+    assert abs(L2[0] - (a + math.log1p(math.exp(b - a)))) < 1e-12
+    assert abs(O2[0, 0] - 1.0 / (1.0 + math.exp(b - a))) < 1e-15
+    Oe, Le = OS.merge_partials(np.zeros((2, 1, 3)), np.full((2, 1), -np.inf))
+    assert np.all(Oe == 0) and np.all(Le == -np.inf)
+
+
 ALL_CHECKS = [
     check_four_token_tiles_consistent,
     check_four_token_recurrence_values,
@@ -339,4 +438,9 @@ ALL_CHECKS = [
     check_against_torch_sdpa,
     check_grouped_heads,
     check_forward_rows,
+    check_cross_square,
+    check_cross_suffix,
+    check_merge_four_token,
+    check_merge_partition,
+    check_merge_properties,
 ]

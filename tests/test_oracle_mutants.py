@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as OA
+import oracle.splitkv as OS
 import oracle_pins
 
 
@@ -114,6 +115,44 @@ def _bwd_group_overwrite(Q, K, V, dO, scale, causal):
 
 
 OA_orig = {name: getattr(OA, name) for name in dir(OA) if not name.startswith("__")}
+OS_orig = {name: getattr(OS, name) for name in dir(OS) if not name.startswith("__")}
+
+
+def _visible_top_left(n_q, n_k, causal, k_begin=0, k_end=None):
+    k_end = n_k if k_end is None else k_end
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    vis = np.broadcast_to((j >= k_begin) & (j < k_end), (n_q, n_k))
+    return vis & (j <= i) if causal else vis
+
+
+def _visible_offset_sign(n_q, n_k, causal, k_begin=0, k_end=None):
+    k_end = n_k if k_end is None else k_end
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    vis = np.broadcast_to((j >= k_begin) & (j < k_end), (n_q, n_k))
+    return vis & (j <= i - (n_k - n_q)) if causal else vis
+
+
+def _visible_range_short(n_q, n_k, causal, k_begin=0, k_end=None):
+    k_end = n_k if k_end is None else k_end
+    return OS_orig["_visible"](n_q, n_k, causal, k_begin, max(k_begin, k_end - 1))
+
+
+def _merge_unnormalised(O_parts, LSE_parts):
+    O_parts, LSE_parts = np.asarray(O_parts, float), np.asarray(LSE_parts, float)
+    w = np.where(np.isfinite(LSE_parts), np.exp(LSE_parts), 0.0)
+    return (w[..., None] * O_parts).sum(axis=0), np.log(w.sum(axis=0))
+
+
+def _merge_lse_max(O_parts, LSE_parts):
+    O, _ = OS_orig["merge_partials"](O_parts, LSE_parts)
+    return O, np.asarray(LSE_parts, float).max(axis=0)
+
+
+def _merge_plain_mean(O_parts, LSE_parts):
+    O, L = OS_orig["merge_partials"](O_parts, LSE_parts)
+    return np.asarray(O_parts, float).mean(axis=0), L
 
 MUTANTS = {
     "scale_dropped": ("_scores", _scores_no_scale),
@@ -132,6 +171,12 @@ MUTANTS = {
     "kv_heads_interleaved": ("kv_head_of", _kv_head_interleaved),
     "rows_causal_off_by_one": ("attention_forward_rows", _rows_off_by_one),
     "group_grads_overwritten": ("attention_backward", _bwd_group_overwrite),
+    "split_causal_top_left": (OS, "_visible", _visible_top_left),
+    "split_causal_offset_sign": (OS, "_visible", _visible_offset_sign),
+    "split_range_drops_last_key": (OS, "_visible", _visible_range_short),
+    "merge_not_normalised": (OS, "merge_partials", _merge_unnormalised),
+    "merge_lse_is_max": (OS, "merge_partials", _merge_lse_max),
+    "merge_ignores_weights": (OS, "merge_partials", _merge_plain_mean),
 }
 
 
@@ -148,7 +193,8 @@ def _caught(check):
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
-    attr, fn = MUTANTS[name]
-    monkeypatch.setattr(OA, attr, fn)
+    spec = MUTANTS[name]
+    mod, attr, fn = spec if len(spec) == 3 else (OA, *spec)
+    monkeypatch.setattr(mod, attr, fn)
     caught = [c.__name__ for c in oracle_pins.ALL_CHECKS if _caught(c)]
     assert caught, f"no pin catches mutant {name}"
