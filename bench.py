@@ -24,6 +24,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 256 CUs x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz = 2516.6
 PEAK_HBM_GBS = 8000.0
+# v_exp_f32 throughput measured on the MI355X with a dependent-free exp loop:
+# 26.5 results per clock per CU; at 256 CUs and 2.4 GHz that is 16.3e12 exp/s.
+EXP_PER_CLK_PER_CU = 26.5
+EXP_RATE = 256 * EXP_PER_CLK_PER_CU * 2.4e9
+COLD_BUFFER_BYTES = 512 << 20  # larger than the 256 MB MALL: writing it evicts the inputs
 
 
 def flops(p, passes):
@@ -74,6 +79,19 @@ def stored_traffic(p):
     return t
 
 
+def exp_count(p):
+    """Exponentials one forward pass evaluates (one per unmasked score, the
+    causal half by the same convention as the FLOP count)."""
+    n = float(p.B) * p.Hq * p.N * p.N
+    return n / 2 if p.causal else n
+
+
+def pct(x, q):
+    """q-th percentile (nearest rank) of a list."""
+    x = sorted(x)
+    return x[min(len(x) - 1, max(0, int(math.ceil(q / 100.0 * len(x))) - 1))]
+
+
 def cpu_baseline(p, passes, budget_s):
     """Time the fp64 oracle on host cores over (b, h) units of the same
     workload until ``budget_s`` of CPU work is done (at least one unit)."""
@@ -111,12 +129,110 @@ def cpu_baseline(p, passes, budget_s):
     }
 
 
+def alg_bytes_split(p):
+    """Algorithmic HBM bytes of one split forward: Q, K, V read once, O and
+    LSE written once (the float32 partials are implementation traffic)."""
+    return 2 * (2 * p.B * p.Hq * p.Nq * p.d + 2 * p.B * p.Hkv * p.Nk * p.d) + 4 * p.B * p.Hq * p.Nq
+
+
+def cpu_baseline_split(p, budget_s):
+    """The fp64 oracle on (b, h_kv-group) units of the split workload."""
+    import numpy as np
+
+    import oracle
+    from io_aware_transformer_amd import inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    G = p.Hq // p.Hkv
+    q, k, v = inputs.make_split(1, G, 1, p.Nq, p.Nk, p.d, p.torch_dtype, p.seed)
+    q, k, v = (t.float().numpy().astype(np.float64) for t in (q, k, v))
+    units = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.cross_forward(q, k, v, p.scale, p.causal)
+        units += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    unit_bytes = alg_bytes_split(p) / (p.B * p.Hkv)
+    return {"value": round(units * unit_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{units} (batch, kv head) units of N_q={p.Nq} x N_k={p.Nk} d={p.d} ({G} query heads each) "
+                      f"in {dt:.1f} s, same algorithmic bytes per unit as the GPU line"}
+
+
+def bench_split(args, p):
+    """Split key/value forward (decoding workloads): one step is one
+    fa_fwd_split call (partials + merge) over the whole batch."""
+    import torch
+
+    from io_aware_transformer_amd import fwd_split, fwd_split_parts, fwd_split_workspace_size, inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inputs.make_split_preset(p))
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(splits, steps, warmup):
+        ws = torch.empty(max(1, fwd_split_workspace_size(p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d, splits)), device=dev,
+                         dtype=torch.uint8)
+        o = torch.empty_like(q)
+        lse = torch.empty((p.B, p.Hq, p.Nq), device=dev, dtype=torch.float32)
+        for _ in range(warmup):
+            fwd_split(q, k, v, scale=p.scale, causal=p.causal, num_splits=splits, out=o, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in evs:
+            e[0].record(stream)
+            fwd_split(q, k, v, scale=p.scale, causal=p.causal, num_splits=splits, out=o, lse=lse, workspace=ws)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return [e[0].elapsed_time(e[1]) for e in evs]
+
+    ms = timed(0, args.steps, args.warmup)
+    avg = sum(ms) / len(ms)
+    gbs = alg_bytes_split(p) / (avg * 1e-3) / 1e9
+    one = timed(1, max(5, args.steps // 5), 2)
+    one_avg = sum(one) / len(one)
+    line = {
+        "metric": "split key/value forward: algorithmic HBM GB/s (bf16, decoding shapes)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(avg, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic: seeded N(0,1) Q, K, V rounded to bf16, resident in HBM",
+        "config": {"workload": f"{p.name}: split fwd {p.dtype} {'causal' if p.causal else 'non-causal'} B={p.B} "
+                               f"H_q={p.Hq} H_kv={p.Hkv} N_q={p.Nq} N_k={p.Nk} d={p.d}",
+                   "parts": fwd_split_parts(p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d, 0)},
+        "ms_p10_p90": [round(pct(ms, 10), 5), round(pct(ms, 90), 5)],
+        "roofline": {"bound": "hbm", "kernel": "fwd_split_kernel + lse_merge_kernel (one fa_fwd_split call)",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "alg_bytes": alg_bytes_split(p)},
+        "unsplit": {"parts": 1, "ms": round(one_avg, 5),
+                    "gbs": round(alg_bytes_split(p) / (one_avg * 1e-3) / 1e9, 1)},
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline_split(p, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--preset", default="c2", help="input preset (default c2: B8 H16 N2048 d128 bf16 causal)")
+    ap.add_argument("--preset", default="c2", help="input preset (default c2: B8 H16 N2048 d128 bf16 causal; "
+                                                    "s1..s3: split key/value forward on decoding shapes)")
     ap.add_argument("--passes", default="fwd,bwd", help="comma list of fwd,bwd")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline budget (0 disables)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -127,6 +243,8 @@ def main():
                          "'write_bytes': W}) to report as roofline.traffic (default: "
                          "profiles/fwd_traffic_<preset>.json when it matches the kernel sources)")
     ap.add_argument("--print-source-hash", action="store_true", help="print the forward sources' sha256 and exit")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="repetitions of the cold-MALL variant (a 512 MB buffer is written before each; 0 disables)")
     args = ap.parse_args()
 
     if args.print_source_hash:
@@ -154,6 +272,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3}), flush=True)
+        return
+    if args.preset in inputs.SPLIT_PRESETS:
+        bench_split(args, inputs.SPLIT_PRESETS[args.preset])
         return
     p = inputs.PRESETS[args.preset]
     passes = [x for x in args.passes.split(",") if x]
@@ -211,6 +332,21 @@ def main():
         x = sorted(x)
         return x[len(x) // 2]
 
+    # Cold-MALL variant: a 512 MB buffer write before every repetition evicts
+    # the inputs from the L2 and MALL, so each pass starts from HBM.
+    cold = None
+    if args.cold_reps > 0:
+        buf = torch.empty(COLD_BUFFER_BYTES // 4, device=dev, dtype=torch.float32)
+        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_reps)]
+        for i in range(args.cold_reps):
+            buf.fill_(float(i))
+            step(cevs[i])
+        torch.cuda.synchronize()
+        cold = {"reps": args.cold_reps, "evict_bytes": COLD_BUFFER_BYTES,
+                "fwd_ms_median": round(med([e[0].elapsed_time(e[1]) for e in cevs]), 5) if "fwd" in passes else None,
+                "bwd_ms_median": round(med([e[1].elapsed_time(e[2]) for e in cevs]), 5) if "bwd" in passes else None}
+        del buf
+
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     fwd_tflops = fwd_flops / (fwd_avg * 1e-3) / 1e12 if "fwd" in passes else None
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
@@ -251,10 +387,14 @@ def main():
     elif p.dtype == "bf16":
         t = stored_traffic(p)
     if t is not None:
-        roofline["traffic"] = {"fetch_bytes": t["fetch_bytes"], "write_bytes": t["write_bytes"],
-                               "total_bytes": t["fetch_bytes"] + t["write_bytes"],
-                               "alg_bytes": alg_bytes_fwd(p), "fetch_factor": t.get("fetch_factor"),
-                               "write_factor": t.get("write_factor"), "source": t.get("source", "")}
+        roofline["traffic"] = t["fetch_bytes"] + t["write_bytes"]
+        roofline["traffic_detail"] = {"fetch_bytes": t["fetch_bytes"], "write_bytes": t["write_bytes"],
+                                      "alg_bytes": alg_bytes_fwd(p), "fetch_factor": t.get("fetch_factor"),
+                                      "write_factor": t.get("write_factor"), "source": t.get("source", "")}
+    if "fwd" in passes and p.dtype == "bf16":
+        # transcendental co-bound: the forward's exponentials at the measured v_exp_f32 rate
+        roofline["exp_bound_ms"] = round(exp_count(p) / EXP_RATE * 1e3, 5)
+        roofline["exp_bound_frac_of_launch"] = round(exp_count(p) / EXP_RATE * 1e3 / fwd_avg, 4)
     line = {
         "metric": "attention fwd/bwd TFLOP/s (bf16, causal, d=128, N=2K-8K) + % MFMA peak",
         "value": round(value, 2),
@@ -277,8 +417,11 @@ def main():
         "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_tflops, 2) if fwd_tflops else None,
         "fwd_ms_median": round(med(fwd_ms), 5),
+        "fwd_ms_p10_p90": [round(pct(fwd_ms, 10), 5), round(pct(fwd_ms, 90), 5)] if "fwd" in passes else None,
         "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
         "bwd_ms_median": round(med(bwd_ms), 5) if "bwd" in passes else None,
+        "bwd_ms_p10_p90": [round(pct(bwd_ms, 10), 5), round(pct(bwd_ms, 90), 5)] if "bwd" in passes else None,
+        "cold_mall": cold,
         "peak_inputs": {"cus": torch.cuda.get_device_properties(dev).multi_processor_count, "sclk_ghz": 2.4,
                         "flop_per_clk_per_cu": 4096},
         "roofline": roofline,

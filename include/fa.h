@@ -72,13 +72,17 @@ enum fa_status {
     FA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required         */
     FA_ERR_UNSUPPORTED = -7, /* valid arguments, no kernel for this combination */
     FA_ERR_HIP = -8,         /* a HIP runtime call failed (fa_last_hip_error)   */
-    FA_ERR_ARG = -9          /* causal not 0/1, or scale not finite             */
+    FA_ERR_ARG = -9          /* causal not 0/1, scale not finite, or a count
+                                out of range                                    */
 };
 
 /* Largest sequence length and head count accepted (index arithmetic in the
  * kernels is 64-bit for element offsets; these bound the grid). */
 #define FA_MAX_N (1 << 22)
 #define FA_MAX_HEADS 65535
+/* Largest number of key ranges (partial results) of the split forward and
+ * of the merge. */
+#define FA_MAX_SPLITS 4096
 
 /*
  * fa_fwd -- forward pass.
@@ -129,6 +133,74 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            void* workspace, size_t workspace_bytes,
            int B, int H_q, int H_kv, int N, int d, float scale, int causal,
            int dtype, void* stream);
+
+/*
+ * Split key/value forward: N_q queries against N_k keys, the keys cut into
+ * ranges whose partial results are merged -- for decoding steps and other
+ * inputs with few queries per head (N_q much smaller than N_k) or few
+ * (batch, head) units, where one workgroup per query block would leave the
+ * GPU idle.
+ *
+ * Partial results over disjoint blocks of keys combine exactly: a block
+ * keeps its maximum and sum of exponentials, and blocks combine by
+ * rescaling to the larger maximum (FlashAttention interview Q&A,
+ * app.wittybyte.ai "FlashAttention1", softmax answer; the same page names
+ * combining partial results of different blocks and incremental attention
+ * among what the method enables).  With a partial kept as
+ * (O_p = its own softmax-weighted V, LSE_p = ln of its sum of exponentials):
+ *     LSE = ln sum_p exp(LSE_p),      O = sum_p exp(LSE_p - LSE) O_p.
+ *
+ * Result: the same attention as fa_fwd, generalised to N_q != N_k:
+ *     Q [B,H_q,N_q,d], K, V [B,H_kv,N_k,d], O [B,H_q,N_q,d], LSE [B,H_q,N_q]
+ * With causal = 1 the queries are the LAST N_q positions of the key
+ * sequence: key j is hidden from query i when j > i + N_k - N_q (a reading;
+ * the pages define no mask).  N_q = N_k gives fa_fwd's mask; N_q = 1 sees
+ * every key.  A query that sees no key (N_q > N_k, causal) gets O = 0 and
+ * LSE = -inf.
+ */
+
+/* Number of key ranges fa_fwd_split uses: num_splits if > 0, else a default
+ * that gives every SIMD of the GPU work; 0 when there is nothing to do or
+ * the arguments are invalid. */
+int fa_fwd_split_parts(int B, int H_q, int H_kv, int N_q, int N_k, int d, int num_splits);
+
+/* Bytes of device workspace fa_fwd_split needs (the float32 partials:
+ * parts x B*H_q*N_q x (d + 1) values, each array 256-byte aligned); 0 when
+ * there is nothing to do or the arguments are invalid. */
+size_t fa_fwd_split_workspace_size(int B, int H_q, int H_kv, int N_q, int N_k, int d, int num_splits, int dtype);
+
+/*
+ * fa_fwd_split -- split key/value forward, then the merge, on ``stream``.
+ *   Q, K, V, O, LSE    as above; LSE may be NULL; all 16-byte aligned
+ *   num_splits         key ranges (0: fa_fwd_split_parts default), at most
+ *                      FA_MAX_SPLITS; ranges past N_k are empty (no cost
+ *                      but their partial, which merges as nothing)
+ *   workspace          at least fa_fwd_split_workspace_size(...) bytes,
+ *                      256-byte aligned; contents on entry are ignored
+ *   B >= 0, N_q >= 0 (B == 0 or N_q == 0: nothing to do, FA_OK), N_k >= 1,
+ *   N_q, N_k <= FA_MAX_N, heads as fa_fwd, causal in {0, 1}, scale finite.
+ *   dtype FA_BF16 and d in {64, 128}; other valid combinations return
+ *   FA_ERR_UNSUPPORTED.
+ */
+int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int B, int H_q, int H_kv, int N_q, int N_k, int d, float scale, int causal,
+                 int num_splits, void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * fa_lse_merge -- merge partial results (the combine step of fa_fwd_split,
+ * also usable for partials computed elsewhere, e.g. on other devices).
+ *   O_parts   float32 [num_parts][rows][d]   each part's output, normalised
+ *                                            by its own sum of exponentials
+ *   LSE_parts float32 [num_parts][rows]      each part's LSE (natural log;
+ *                                            -inf: the part saw no key)
+ *   O         [rows][d] of dtype (FA_BF16 or FA_FP32)    output
+ *   LSE       float32 [rows]                 output, may be NULL
+ *   1 <= num_parts <= FA_MAX_SPLITS, rows >= 0 (0: nothing to do),
+ *   d in {64, 128, 256}; pointers 16-byte aligned.  A row whose parts are
+ *   all -inf gets O = 0, LSE = -inf.
+ */
+int fa_lse_merge(const float* O_parts, const float* LSE_parts, int num_parts, long long rows, int d,
+                 void* O, float* LSE, int dtype, void* stream);
 
 /* Name of a status code ("FA_OK", "FA_ERR_SHAPE", ...); never NULL. */
 const char* fa_status_str(int status);

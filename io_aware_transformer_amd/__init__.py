@@ -2,11 +2,13 @@
 
 The computation lives in hand-written HIP kernels behind the C ABI of
 ``include/fa.h`` (``libfa.so``); this package only marshals torch tensors
-into that ABI.  ``fwd``/``bwd`` raise ``LibraryNotBuilt`` when the library
+into that ABI.  ``fwd``/``bwd`` (and the split key/value forward ``fwd_split`` with its
+merge ``lse_merge``) raise ``LibraryNotBuilt`` when the library
 is missing -- there is no fallback path.
 """
 
 from ._lib import FA_BF16, FA_FP32, FAError, LibraryNotBuilt, load as load_library
-from .attention import bwd, bwd_workspace_size, fwd
+from .attention import bwd, bwd_workspace_size, fwd, fwd_split, fwd_split_parts, fwd_split_workspace_size, lse_merge
 
-__all__ = ["fwd", "bwd", "bwd_workspace_size", "FAError", "LibraryNotBuilt", "load_library", "FA_BF16", "FA_FP32"]
+__all__ = ["fwd", "bwd", "bwd_workspace_size", "fwd_split", "fwd_split_parts", "fwd_split_workspace_size",
+           "lse_merge", "FAError", "LibraryNotBuilt", "load_library", "FA_BF16", "FA_FP32"]

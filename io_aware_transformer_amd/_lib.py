@@ -36,6 +36,10 @@ EXPORTS = (
     "fa_status_str",
     "fa_last_hip_error",
     "fa_version",
+    "fa_fwd_split_parts",
+    "fa_fwd_split_workspace_size",
+    "fa_fwd_split",
+    "fa_lse_merge",
 )
 
 
@@ -81,6 +85,14 @@ def load():
     lib.fa_last_hip_error.restype = _i
     lib.fa_version.argtypes = []
     lib.fa_version.restype = _i
+    lib.fa_fwd_split_parts.argtypes = [_i] * 7
+    lib.fa_fwd_split_parts.restype = _i
+    lib.fa_fwd_split_workspace_size.argtypes = [_i] * 8
+    lib.fa_fwd_split_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_split.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _i, _vp, ctypes.c_size_t, _i, _vp]
+    lib.fa_fwd_split.restype = _i
+    lib.fa_lse_merge.argtypes = [_vp, _vp, _i, ctypes.c_longlong, _i, _vp, _vp, _i, _vp]
+    lib.fa_lse_merge.restype = _i
     _lib = lib
     return lib
 

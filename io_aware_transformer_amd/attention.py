@@ -82,3 +82,80 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=True, workspace=None):
     )
     _lib.check(st, "fa_bwd")
     return dq, dk, dv
+
+
+def _check_split(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if not q.is_cuda:
+        raise ValueError("tensors must be on a HIP device")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t in (k, v):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on the same device")
+        if t.dtype != q.dtype:
+            raise TypeError("all tensors must share one dtype")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k, v must be [B, H_kv, N_k, d] matching q")
+    return B, Hq, k.shape[1], Nq, k.shape[2], d
+
+
+def fwd_split_parts(B, Hq, Hkv, Nq, Nk, d, num_splits=0):
+    return int(_lib.load().fa_fwd_split_parts(B, Hq, Hkv, Nq, Nk, d, int(num_splits)))
+
+
+def fwd_split_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits=0, dtype=torch.bfloat16):
+    return int(_lib.load().fa_fwd_split_workspace_size(B, Hq, Hkv, Nq, Nk, d, int(num_splits), _DTYPES[dtype]))
+
+
+def fwd_split(q, k, v, scale=None, causal=True, num_splits=0, out=None, lse=None, workspace=None):
+    """Split key/value forward: q [B, H_q, N_q, d] against k, v [B, H_kv, N_k, d].
+
+    Returns (o like q, lse float32 [B, H_q, N_q]).  ``num_splits`` key
+    ranges (0: the library's default); causal aligns the queries with the
+    last N_q key positions.
+    """
+    B, Hq, Hkv, Nq, Nk, d = _check_split(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
+    ws_bytes = fwd_split_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    lib = _lib.load()
+    st = lib.fa_fwd_split(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        lse.data_ptr() or None, B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(num_splits),
+        workspace.data_ptr() or None, workspace.numel(), _DTYPES[q.dtype], _stream(q.device),
+    )
+    _lib.check(st, "fa_fwd_split")
+    return o, lse
+
+
+def lse_merge(o_parts, lse_parts, dtype=torch.bfloat16, out=None, lse=None):
+    """Merge partial results: o_parts float32 [P, ..., d], lse_parts float32
+    [P, ...] -> (o [..., d] of ``dtype``, lse float32 [...])."""
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if not (o_parts.is_cuda and lse_parts.is_cuda and o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("partials must be contiguous device tensors")
+    if o_parts.shape[:-1] != lse_parts.shape or o_parts.dim() < 2:
+        raise ValueError("o_parts must be [P, ..., d] and lse_parts [P, ...]")
+    P, d = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    o = torch.empty(o_parts.shape[1:], device=o_parts.device, dtype=dtype) if out is None else out
+    if lse is None:
+        lse = torch.empty(lse_parts.shape[1:], device=o_parts.device, dtype=torch.float32)
+    st = _lib.load().fa_lse_merge(
+        o_parts.data_ptr() or None, lse_parts.data_ptr() or None, P, rows, d, o.data_ptr() or None,
+        lse.data_ptr() or None, _DTYPES[dtype], _stream(o_parts.device),
+    )
+    _lib.check(st, "fa_lse_merge")
+    return o, lse

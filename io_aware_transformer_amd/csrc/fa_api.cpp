@@ -35,11 +35,38 @@ int validate(int B, int Hq, int Hkv, int N, int d, float scale, int causal, int 
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Checks of the split forward: N_q queries against N_k keys.
+int validate_split(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, int splits) {
+    if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_DTYPE;
+    if (B < 0 || Nq < 0 || Nk < 0 || Nq > FA_MAX_N || Nk > FA_MAX_N) return FA_ERR_SHAPE;
+    if (Hq < 1 || Hkv < 1 || Hq > FA_MAX_HEADS || Hkv > Hq || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_ARG;
+    if (splits < 0 || splits > FA_MAX_SPLITS) return FA_ERR_ARG;
+    if (B > 0 && Nq > 0 && Nk == 0) return FA_ERR_SHAPE;  // attention over no keys is undefined
+    return FA_OK;
+}
+
+// Resolved number of key ranges (0 = the default for these sizes), or 0 when
+// there is nothing to do.
+int split_parts(int B, int Hq, int Hkv, int Nq, int Nk, int d, int splits) {
+    if (B == 0 || Nq == 0) return 0;
+    return splits > 0 ? splits : fa::split_parts_default(B, Hq, Hkv, Nq, Nk, d);
+}
+
+bool split_grid_ok(int B, int Hq, int Hkv, int Nq, int parts) {
+    const long long rows = (long long)(Hq / Hkv) * Nq;
+    const long long blocks = (long long)B * Hkv * ((rows + 31) / 32) * parts;  // at one wave per workgroup
+    const long long merge_rows = (long long)B * Hq * Nq;
+    return blocks <= (long long)INT_MAX && merge_rows <= (long long)INT_MAX * 4;
+}
+
 }  // namespace
 
 extern "C" {
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 110; }
 
 const char* fa_status_str(int status) {
     switch (status) {
@@ -123,6 +150,71 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = (dtype == FA_BF16) ? fa::launch_bwd_bf16(p, d, causal, s) : fa::launch_bwd_f32(p, d, causal, s);
     if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
+    if (e != hipSuccess) return hip_failure(e);
+    return FA_OK;
+}
+
+size_t fa_fwd_split_workspace_size(int B, int H_q, int H_kv, int N_q, int N_k, int d, int num_splits, int dtype) {
+    if (validate_split(B, H_q, H_kv, N_q, N_k, d, 1.0f, 0, dtype, num_splits) != FA_OK) return 0;
+    const int parts = split_parts(B, H_q, H_kv, N_q, N_k, d, num_splits);
+    if (parts == 0) return 0;
+    return fa::split_workspace_bytes(B, H_q, N_q, d, parts);
+}
+
+int fa_fwd_split_parts(int B, int H_q, int H_kv, int N_q, int N_k, int d, int num_splits) {
+    if (validate_split(B, H_q, H_kv, N_q, N_k, d, 1.0f, 0, FA_BF16, num_splits) != FA_OK) return 0;
+    return split_parts(B, H_q, H_kv, N_q, N_k, d, num_splits);
+}
+
+int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N_q,
+                 int N_k, int d, float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes,
+                 int dtype, void* stream) {
+    int st = validate_split(B, H_q, H_kv, N_q, N_k, d, scale, causal, dtype, num_splits);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16 || d == 256) return FA_ERR_UNSUPPORTED;
+    const int parts = split_parts(B, H_q, H_kv, N_q, N_k, d, num_splits);
+    if (parts == 0) return FA_OK;
+    if (!split_grid_ok(B, H_q, H_kv, N_q, parts)) return FA_ERR_SHAPE;
+    if (!Q || !K || !V || !O) return FA_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 16))
+        return FA_ERR_ALIGN;
+    const size_t need = fa::split_workspace_bytes(B, H_q, N_q, d, parts);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
+    const long long rows = (long long)B * H_q * N_q;
+    fa::SplitParams p{};
+    p.Q = Q;
+    p.K = K;
+    p.V = V;
+    p.Opart = static_cast<float*>(workspace);
+    p.LSEpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         (size_t(parts) * size_t(rows) * d * sizeof(float) + 255) / 256 * 256);
+    p.B = B;
+    p.Hq = H_q;
+    p.Hkv = H_kv;
+    p.Nq = N_q;
+    p.Nk = N_k;
+    p.scale_log2 = scale * kLog2e;
+    p.parts = parts;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = fa::launch_fwd_split_bf16(p, d, causal, s);
+    if (e == hipSuccess) e = fa::launch_lse_merge(p.Opart, p.LSEpart, parts, rows, d, O, LSE, 1, s);
+    if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
+    if (e != hipSuccess) return hip_failure(e);
+    return FA_OK;
+}
+
+int fa_lse_merge(const float* O_parts, const float* LSE_parts, int num_parts, long long rows, int d, void* O,
+                 float* LSE, int dtype, void* stream) {
+    if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+    if (num_parts < 1 || num_parts > FA_MAX_SPLITS) return FA_ERR_ARG;
+    if (rows < 0 || rows > (long long)INT_MAX * 4) return FA_ERR_SHAPE;
+    if (rows == 0) return FA_OK;
+    if (!O_parts || !LSE_parts || !O) return FA_ERR_NULL;
+    if (!aligned(O_parts, 16) || !aligned(LSE_parts, 16) || !aligned(O, 16) || !aligned(LSE, 16)) return FA_ERR_ALIGN;
+    hipError_t e = fa::launch_lse_merge(O_parts, LSE_parts, num_parts, rows, d, O, LSE, dtype == FA_BF16,
+                                        static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_failure(e);
     return FA_OK;
 }

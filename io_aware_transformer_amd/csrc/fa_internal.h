@@ -39,6 +39,23 @@ struct BwdParams {
     int nqb, nkb;      // query / key blocks (filled by the launchers)
 };
 
+// Split key/value forward parameters.  Q [B, Hq, Nq, d], K/V [B, Hkv, Nk, d]
+// (bf16); the partials go to Opart fp32 [parts][B*Hq*Nq][d] and LSEpart fp32
+// [parts][B*Hq*Nq].
+struct SplitParams {
+    const void* Q;
+    const void* K;
+    const void* V;
+    float* Opart;
+    float* LSEpart;
+    int B, Hq, Hkv, Nq, Nk;
+    float scale_log2;
+    int parts;  // key ranges
+    int qmode;  // filled by the launcher (as FwdParams::qmode)
+    int chunk;  // keys per range, a multiple of 32 (filled by the launcher)
+    int nrb;    // blocks of 32 packed rows per kv head (filled by the launcher)
+};
+
 // Each launcher enqueues its kernels on `stream` and returns the first HIP
 // error (hipSuccess when everything was enqueued).  Shapes were validated
 // by the caller; d is one of the supported head dims for that launcher.
@@ -49,5 +66,15 @@ hipError_t launch_bwd_f32(BwdParams p, int d, int causal, hipStream_t stream);
 
 // Workspace bytes of the backward for these sizes (D term only).
 size_t bwd_workspace_bytes(int B, int Hq, int N);
+
+// Split forward: partial kernel (launch_fwd_split_bf16, d in {64, 128}) and
+// the merge of partials (launch_lse_merge, d in {64, 128, 256}, output bf16
+// when out_bf16 else float32).
+hipError_t launch_fwd_split_bf16(SplitParams p, int d, int causal, hipStream_t stream);
+hipError_t launch_lse_merge(const float* Opart, const float* LSEpart, int parts, long long rows, int d, void* O,
+                            float* LSE, int out_bf16, hipStream_t stream);
+int split_parts_default(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+int split_chunk(int Nk, int parts);
+size_t split_workspace_bytes(int B, int Hq, int Nq, int d, int parts);
 
 }  // namespace fa

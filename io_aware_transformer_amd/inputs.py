@@ -4,8 +4,9 @@ attention arithmetic lives here.
 
 Recipe: a CPU ``torch.Generator`` seeded with the preset's seed draws
 standard-normal float32 tensors in the order Q, K, V, dO (each contiguous
-[B, H, N, d]; K and V use H_kv heads); bf16 presets round those values to
-bfloat16 (round to nearest even).  The same rounded values feed the GPU and,
+[B, H, N, d]; K and V use H_kv heads; for the split presets Q has N_q rows
+and K, V have N_k); bf16 presets round those values to bfloat16 (round to
+nearest even).  The same rounded values feed the GPU and,
 upcast exactly to float64, the oracle.
 """
 
@@ -66,6 +67,60 @@ def make(B, Hq, Hkv, N, d, dtype=torch.bfloat16, seed=0, with_grad=False):
     if with_grad:
         out.append(torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32))
     return tuple(t.to(dtype) for t in out)
+
+
+@dataclass(frozen=True)
+class SplitPreset:
+    """N_q queries against N_k keys (split key/value forward workloads)."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+    dtype: str = "bf16"
+
+    @property
+    def scale(self):
+        return self.d ** -0.5
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def describe(self):
+        return (f"{self.name}: B={self.B} H_q={self.Hq} H_kv={self.Hkv} N_q={self.Nq} N_k={self.Nk} d={self.d} "
+                f"{self.dtype} {'causal' if self.causal else 'non-causal'} seed={self.seed}")
+
+
+# Decoding steps (one query per head against a long key/value cache), with
+# grouped heads (4 query heads per kv head) and without.
+SPLIT_PRESETS = {
+    p.name: p
+    for p in [
+        SplitPreset("s1", 4, 32, 8, 1, 16384, 128, True, 601),
+        SplitPreset("s2", 8, 16, 16, 1, 8192, 128, True, 602),
+        SplitPreset("s3", 1, 8, 8, 16, 32768, 64, True, 603),
+    ]
+}
+
+
+def make_split(B, Hq, Hkv, Nq, Nk, d, dtype=torch.bfloat16, seed=0):
+    """Q [B, Hq, Nq, d], K and V [B, Hkv, Nk, d], drawn in that order."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, Hq, Nq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32)
+    return tuple(t.to(dtype) for t in (q, k, v))
+
+
+def make_split_preset(p):
+    return make_split(p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d, p.torch_dtype, p.seed)
 
 
 def make_preset(p, with_grad=None):

@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code, name in _lib.STATUS.items():
         assert lib.fa_status_str(code).decode() == name
     assert lib.fa_status_str(12345).decode() == "FA_ERR_UNKNOWN"
-    assert lib.fa_version() == 100
+    assert lib.fa_version() == 110
     assert lib.fa_last_hip_error() == 0
 
 
@@ -132,3 +132,81 @@ def test_workspace_size_formula():
 
 def test_bwd_empty_is_noop():
     assert bwd(Q=None, K=None, V=None, O=None, dO=None, LSE=None, dQ=None, dK=None, dV=None, ws=None, N=0) == 0
+
+
+def split(ws_bytes=1 << 24, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, ws=0x100000, B=2, Hq=8, Hkv=2, Nq=1, Nk=1000, d=128,
+             scale=0.09, causal=1, splits=0, dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_fwd_split(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                    a["Nk"], a["d"], a["scale"], a["causal"], a["splits"], a["ws"], ws_bytes,
+                                    a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), "FA_ERR_NULL"),
+    (dict(O=None), "FA_ERR_NULL"),
+    (dict(Nk=0), "FA_ERR_SHAPE"),
+    (dict(Nq=-1), "FA_ERR_SHAPE"),
+    (dict(Nk=(1 << 22) + 1), "FA_ERR_SHAPE"),
+    (dict(Hq=6, Hkv=4), "FA_ERR_SHAPE"),
+    (dict(d=80), "FA_ERR_HEADDIM"),
+    (dict(d=256), "FA_ERR_UNSUPPORTED"),
+    (dict(dtype=_lib.FA_FP32), "FA_ERR_UNSUPPORTED"),
+    (dict(dtype=3), "FA_ERR_DTYPE"),
+    (dict(splits=-1), "FA_ERR_ARG"),
+    (dict(splits=4097), "FA_ERR_ARG"),
+    (dict(causal=5), "FA_ERR_ARG"),
+    (dict(K=MIS), "FA_ERR_ALIGN"),
+    (dict(ws=0x100040), "FA_ERR_ALIGN"),
+    (dict(ws=None), "FA_ERR_WORKSPACE"),
+])
+def test_split_rejects(kw, code):
+    assert split(**kw) == E[code]
+
+
+def test_split_workspace_and_parts():
+    lib = _lib.load()
+    # explicit splits: parts x rows x (d + 1) floats, each array rounded to 256 bytes
+    rows = 2 * 8 * 3
+    want = (7 * rows * 128 * 4 + 255) // 256 * 256 + (7 * rows * 4 + 255) // 256 * 256
+    assert lib.fa_fwd_split_parts(2, 8, 2, 3, 1000, 128, 7) == 7
+    assert lib.fa_fwd_split_workspace_size(2, 8, 2, 3, 1000, 128, 7, _lib.FA_BF16) == want
+    # default: one workgroup per compute unit (3 waves at d = 128, 4 at d = 64),
+    # at least 4 tiles of 32 keys per part
+    assert lib.fa_fwd_split_parts(4, 32, 8, 1, 16384, 128, 0) == 24
+    assert lib.fa_fwd_split_parts(4, 32, 8, 1, 16384, 64, 0) == 32
+    assert lib.fa_fwd_split_parts(1, 1, 1, 1, 100, 64, 0) == 1
+    assert lib.fa_fwd_split_parts(0, 8, 2, 1, 100, 64, 0) == 0
+    assert lib.fa_fwd_split_workspace_size(2, 8, 2, 0, 1000, 128, 3, _lib.FA_BF16) == 0
+    need = lib.fa_fwd_split_workspace_size(2, 8, 2, 1, 1000, 128, 0, _lib.FA_BF16)
+    assert split(ws_bytes=need - 1) == E["FA_ERR_WORKSPACE"]
+
+
+def test_split_empty_is_noop():
+    assert split(Q=None, K=None, V=None, O=None, LSE=None, ws=None, Nq=0) == 0
+    assert split(Q=None, K=None, V=None, O=None, LSE=None, ws=None, B=0) == 0
+
+
+def merge(**kw):
+    a = dict(Op=FAKE, Lp=FAKE, parts=3, rows=10, d=128, O=FAKE, LSE=FAKE, dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_lse_merge(a["Op"], a["Lp"], a["parts"], a["rows"], a["d"], a["O"], a["LSE"], a["dtype"],
+                                    None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Op=None), "FA_ERR_NULL"),
+    (dict(O=None), "FA_ERR_NULL"),
+    (dict(parts=0), "FA_ERR_ARG"),
+    (dict(rows=-1), "FA_ERR_SHAPE"),
+    (dict(d=32), "FA_ERR_HEADDIM"),
+    (dict(dtype=9), "FA_ERR_DTYPE"),
+    (dict(Lp=MIS), "FA_ERR_ALIGN"),
+])
+def test_merge_rejects(kw, code):
+    assert merge(**kw) == E[code]
+
+
+def test_merge_empty_is_noop():
+    assert merge(Op=None, Lp=None, O=None, LSE=None, rows=0) == 0
