@@ -10,9 +10,10 @@ The oracle is the plain definition of attention (materialise the score
 matrix, stable row softmax, multiply by V) and the textbook analytic
 backward, in float64, one (batch, query-head) unit at a time, plus
 attention with queries and keys of different lengths, attention over a key
-range, and the merge of partial results over disjoint key ranges.  Every
+range, the merge of partial results over disjoint key ranges, and local
+(sliding-window) attention.  Every
 function cites the passage of the source pages it follows; see
-``oracle/attention.py`` and ``oracle/splitkv.py``.
+``oracle/attention.py``, ``oracle/splitkv.py`` and ``oracle/window.py``.
 """
 
 from .attention import (
@@ -24,6 +25,7 @@ from .attention import (
     kv_head_of,
 )
 from .splitkv import cross_forward, merge_partials, partial_forward
+from .window import window_backward, window_forward, window_visible
 
 __all__ = [
     "attention_forward",
@@ -35,4 +37,7 @@ __all__ = [
     "cross_forward",
     "partial_forward",
     "merge_partials",
+    "window_forward",
+    "window_backward",
+    "window_visible",
 ]

@@ -18,6 +18,7 @@ import numpy as np
 
 import oracle.attention as OA
 import oracle.splitkv as OS
+import oracle.window as OW
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -424,6 +425,75 @@ def check_merge_properties(seed=20):
     assert np.all(Oe == 0) and np.all(Le == -np.inf)
 
 
+# ---------------------------------------------------------------- windows
+
+
+def check_window_special_cases(seed=21):
+    """(-1, 0) is the causal mask and (-1, -1) no mask, forward and backward;
+    (0, 0) lets every row see only its own key: O = V, LSE = its own score,
+    dV = dO and dQ = dK = 0."""
+    rng = np.random.default_rng(seed)
+    Q, K, V = _qkv(rng, 2, 4, 2, 10, 10, 6)
+    dO = rng.standard_normal(Q.shape)
+    for (lw, rw), causal in (((-1, 0), True), ((-1, -1), False)):
+        O, L = OW.window_forward(Q, K, V, 0.4, lw, rw)
+        Or, Lr = OA.attention_forward(Q, K, V, 0.4, causal)
+        assert np.max(np.abs(O - Or)) < 1e-14 and np.max(np.abs(L - Lr)) < 1e-13
+        g = OW.window_backward(Q, K, V, dO, 0.4, lw, rw)
+        gr = OA.attention_backward(Q, K, V, dO, 0.4, causal)
+        for a, b in zip(g, gr):
+            assert np.max(np.abs(a - b)) < 1e-12
+    O, L = OW.window_forward(Q, K, V, 0.4, 0, 0)
+    G = Q.shape[1] // K.shape[1]
+    Vr = np.repeat(V, G, axis=1)
+    Kr = np.repeat(K, G, axis=1)
+    assert np.max(np.abs(O - Vr)) < 1e-15
+    assert np.max(np.abs(L - 0.4 * (Q * Kr).sum(axis=3))) < 1e-13
+    dQ, dK, dV = OW.window_backward(Q, K, V, dO, 0.4, 0, 0)
+    assert np.max(np.abs(dQ)) < 1e-15 and np.max(np.abs(dK)) < 1e-15
+    assert np.max(np.abs(dV - dO.reshape(2, 2, G, 10, 6).sum(axis=2))) < 1e-14
+
+
+def check_window_rows_are_slices(seed=22):
+    """Row i of a (left, right) window is plain attention of query i over the
+    keys i-left .. i+right (clipped), computed with the square definition on
+    that slice."""
+    rng = np.random.default_rng(seed)
+    n = 17
+    Q, K, V = _qkv(rng, 1, 1, 1, n, n, 5)
+    for lw, rw in ((3, 0), (0, 2), (4, 5), (-1, 3), (6, -1)):
+        O, L = OW.window_forward(Q, K, V, 0.6, lw, rw)
+        for i in range(n):
+            a = 0 if lw < 0 else max(0, i - lw)
+            b = n if rw < 0 else min(n, i + rw + 1)
+            o, l = OA.head_forward(Q[0, 0, i:i + 1], K[0, 0, a:b], V[0, 0, a:b], 0.6, False)
+            assert np.max(np.abs(O[0, 0, i] - o[0])) < 1e-14 and abs(L[0, 0, i] - l[0]) < 1e-13
+
+
+def check_window_finite_differences(seed=23):
+    """Central differences of <dO, O> for a two-sided window."""
+    rng = np.random.default_rng(seed)
+    Q, K, V = _qkv(rng, 1, 2, 1, 7, 7, 3)
+    dO = rng.standard_normal(Q.shape)
+    lw, rw, sc = 2, 1, 0.8
+    dQ, dK, dV = OW.window_backward(Q, K, V, dO, sc, lw, rw)
+    h = 1e-6
+
+    def loss(q, k, v):
+        return float((OW.window_forward(q, k, v, sc, lw, rw)[0] * dO).sum())
+
+    for X, G in ((Q, dQ), (K, dK), (V, dV)):
+        idx = [tuple(rng.integers(0, s) for s in X.shape) for _ in range(6)]
+        for ix in idx:
+            Xp, Xm = X.copy(), X.copy()
+            Xp[ix] += h
+            Xm[ix] -= h
+            args_p = [Xp if Y is X else Y for Y in (Q, K, V)]
+            args_m = [Xm if Y is X else Y for Y in (Q, K, V)]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - G[ix]) < 1e-7 * max(1.0, abs(fd)), (ix, fd, G[ix])
+
+
 ALL_CHECKS = [
     check_four_token_tiles_consistent,
     check_four_token_recurrence_values,
@@ -443,4 +513,7 @@ ALL_CHECKS = [
     check_merge_four_token,
     check_merge_partition,
     check_merge_properties,
+    check_window_special_cases,
+    check_window_rows_are_slices,
+    check_window_finite_differences,
 ]

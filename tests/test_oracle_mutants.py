@@ -9,6 +9,7 @@ import pytest
 
 import oracle.attention as OA
 import oracle.splitkv as OS
+import oracle.window as OW
 import oracle_pins
 
 
@@ -116,6 +117,7 @@ def _bwd_group_overwrite(Q, K, V, dO, scale, causal):
 
 OA_orig = {name: getattr(OA, name) for name in dir(OA) if not name.startswith("__")}
 OS_orig = {name: getattr(OS, name) for name in dir(OS) if not name.startswith("__")}
+OW_orig = {name: getattr(OW, name) for name in dir(OW) if not name.startswith("__")}
 
 
 def _visible_top_left(n_q, n_k, causal, k_begin=0, k_end=None):
@@ -137,6 +139,37 @@ def _visible_offset_sign(n_q, n_k, causal, k_begin=0, k_end=None):
 def _visible_range_short(n_q, n_k, causal, k_begin=0, k_end=None):
     k_end = n_k if k_end is None else k_end
     return OS_orig["_visible"](n_q, n_k, causal, k_begin, max(k_begin, k_end - 1))
+
+
+def _window_off_by_one(n, left, right):
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    vis = np.ones((n, n), dtype=bool)
+    if left >= 0:
+        vis &= j > i - left
+    if right >= 0:
+        vis &= j <= i + right
+    return vis
+
+
+def _window_swapped(n, left, right):
+    return OW_orig["window_visible"](n, right, left)
+
+
+def _window_bwd_no_rowterm(Q, K, V, dO, scale, left, right):
+    Q, K, V, dO = (np.asarray(x, float) for x in (Q, K, V, dO))
+    B, Hq, Hkv, N, d = OA._check_shapes(Q, K, V)
+    vis = OW.window_visible(N, left, right)
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = OA.kv_head_of(h, Hq, Hkv)
+            p, _, _ = OW._head_probs(Q[b, h], K[b, g], scale, vis)
+            ds = p * (dO[b, h] @ V[b, g].T)
+            dQ[b, h] = scale * (ds @ K[b, g])
+            dK[b, g] += scale * (ds.T @ Q[b, h])
+            dV[b, g] += p.T @ dO[b, h]
+    return dQ, dK, dV
 
 
 def _merge_unnormalised(O_parts, LSE_parts):
@@ -177,6 +210,9 @@ MUTANTS = {
     "merge_not_normalised": (OS, "merge_partials", _merge_unnormalised),
     "merge_lse_is_max": (OS, "merge_partials", _merge_lse_max),
     "merge_ignores_weights": (OS, "merge_partials", _merge_plain_mean),
+    "window_left_off_by_one": (OW, "window_visible", _window_off_by_one),
+    "window_sides_swapped": (OW, "window_visible", _window_swapped),
+    "window_bwd_missing_row_term": (OW, "window_backward", _window_bwd_no_rowterm),
 }
 
 
