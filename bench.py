@@ -79,6 +79,16 @@ def stored_traffic(p):
     return t
 
 
+def window_pairs(n, left, right):
+    """Number of (query, key) pairs a window (left, right) leaves visible."""
+    total = 0
+    for i in range(n):
+        a = 0 if left < 0 else max(0, i - left)
+        b = n - 1 if right < 0 else min(n - 1, i + right)
+        total += b - a + 1
+    return total
+
+
 def exp_count(p):
     """Exponentials one forward pass evaluates (one per unmasked score, the
     causal half by the same convention as the FLOP count)."""
@@ -243,6 +253,9 @@ def main():
                          "'write_bytes': W}) to report as roofline.traffic (default: "
                          "profiles/fwd_traffic_<preset>.json when it matches the kernel sources)")
     ap.add_argument("--print-source-hash", action="store_true", help="print the forward sources' sha256 and exit")
+    ap.add_argument("--window", default=None,
+                    help="LEFT,RIGHT: local attention (query i sees keys i-LEFT .. i+RIGHT, -1 unbounded) through "
+                         "fa_fwd_window / fa_bwd_window; FLOP counted over the visible (query, key) pairs")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="repetitions of the cold-MALL variant (a 512 MB buffer is written before each; 0 disables)")
     args = ap.parse_args()
@@ -278,6 +291,17 @@ def main():
         return
     p = inputs.PRESETS[args.preset]
     passes = [x for x in args.passes.split(",") if x]
+
+    window = None
+    if args.window:
+        window = tuple(int(x) for x in args.window.split(","))
+        from io_aware_transformer_amd import bwd_window, fwd_window
+
+        def fwd(q, k, v, scale, causal, out=None, lse=None):  # noqa: F811 -- same call shape as the causal pass
+            return fwd_window(q, k, v, window, scale=scale, out=out, lse=lse)
+
+        def bwd(q, k, v, o, lse, do, scale, causal, workspace=None):  # noqa: F811
+            return bwd_window(q, k, v, o, lse, do, window, scale=scale, workspace=workspace)
 
     q, k, v, do = (t.to(dev) for t in inputs.make_preset(p, with_grad=True))
     o, lse = fwd(q, k, v, scale=p.scale, causal=p.causal)
@@ -326,6 +350,9 @@ def main():
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
     ms_per_step = total_ms / args.steps
     total_flops, fwd_flops = flops(p, passes)
+    if window is not None:
+        fwd_flops = 4.0 * p.B * p.Hq * p.d * window_pairs(p.N, *window)
+        total_flops = fwd_flops * (("fwd" in passes) + 2.5 * ("bwd" in passes))
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
     def med(x):
@@ -393,8 +420,9 @@ def main():
                                       "write_factor": t.get("write_factor"), "source": t.get("source", "")}
     if "fwd" in passes and p.dtype == "bf16":
         # transcendental co-bound: the forward's exponentials at the measured v_exp_f32 rate
-        roofline["exp_bound_ms"] = round(exp_count(p) / EXP_RATE * 1e3, 5)
-        roofline["exp_bound_frac_of_launch"] = round(exp_count(p) / EXP_RATE * 1e3 / fwd_avg, 4)
+        n_exp = exp_count(p) if window is None else float(p.B) * p.Hq * window_pairs(p.N, *window)
+        roofline["exp_bound_ms"] = round(n_exp / EXP_RATE * 1e3, 5)
+        roofline["exp_bound_frac_of_launch"] = round(n_exp / EXP_RATE * 1e3 / fwd_avg, 4)
     line = {
         "metric": "attention fwd/bwd TFLOP/s (bf16, causal, d=128, N=2K-8K) + % MFMA peak",
         "value": round(value, 2),
@@ -409,8 +437,10 @@ def main():
         "dtype": p.dtype,
         "data": "synthetic: seeded N(0,1) Q, K, V, dO rounded to bf16, resident in HBM",
         "config": {
-            "workload": f"{p.name}: {'+'.join(passes)} {p.dtype} {'causal' if p.causal else 'non-causal'} "
+            "workload": f"{p.name}: {'+'.join(passes)} {p.dtype} "
+                        f"{('window ' + args.window) if window else ('causal' if p.causal else 'non-causal')} "
                         f"attention B={p.B} H_q={p.Hq} H_kv={p.Hkv} N={p.N} d={p.d}",
+            "window": list(window) if window else None,
             "B": p.B, "H_q": p.Hq, "H_kv": p.Hkv, "N": p.N, "d": p.d, "causal": p.causal,
             "passes": passes, "parallelism": "single GPU",
         },
@@ -427,7 +457,7 @@ def main():
         "roofline": roofline,
         "roofline_bwd": roofline_bwd,
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and window is None:
         line["cpu_baseline"] = cpu_baseline(p, passes, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

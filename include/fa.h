@@ -135,6 +135,32 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            int dtype, void* stream);
 
 /*
+ * Local (sliding-window) attention.  The pages name local and sparse
+ * attention as a combination with the method (FlashAttention interview Q&A,
+ * app.wittybyte.ai "FlashAttention1": sparse attention such as local
+ * attention for very long sequences; sparse FlashAttention as a future
+ * direction) but define no pattern.  Reading: with the window
+ * (window_left, window_right), query i sees key j exactly when
+ *     i - window_left <= j <= i + window_right,
+ * -1 meaning unbounded on that side: (-1, 0) is fa_fwd's causal mask,
+ * (-1, -1) no mask.  Every row sees at least its own key.  Key tiles wholly
+ * outside a query block's windows are not visited.
+ *
+ * fa_fwd_window / fa_bwd_window -- as fa_fwd / fa_bwd with the window in
+ * place of the causal flag; window_left, window_right >= -1 (else
+ * FA_ERR_ARG).  fa_bwd_window must get O and LSE of fa_fwd_window with the
+ * same window.  Same shapes, dtypes and constraints as fa_fwd / fa_bwd.
+ */
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                  int B, int H_q, int H_kv, int N, int d, float scale,
+                  int window_left, int window_right, int dtype, void* stream);
+int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O,
+                  const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int H_q, int H_kv, int N, int d, float scale,
+                  int window_left, int window_right, int dtype, void* stream);
+
+/*
  * Split key/value forward: N_q queries against N_k keys, the keys cut into
  * ranges whose partial results are merged -- for decoding steps and other
  * inputs with few queries per head (N_q much smaller than N_k) or few

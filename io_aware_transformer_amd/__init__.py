@@ -8,7 +8,8 @@ is missing -- there is no fallback path.
 """
 
 from ._lib import FA_BF16, FA_FP32, FAError, LibraryNotBuilt, load as load_library
-from .attention import bwd, bwd_workspace_size, fwd, fwd_split, fwd_split_parts, fwd_split_workspace_size, lse_merge
+from .attention import (bwd, bwd_window, bwd_workspace_size, fwd, fwd_split, fwd_split_parts, fwd_split_workspace_size,
+                        fwd_window, lse_merge)
 
 __all__ = ["fwd", "bwd", "bwd_workspace_size", "fwd_split", "fwd_split_parts", "fwd_split_workspace_size",
-           "lse_merge", "FAError", "LibraryNotBuilt", "load_library", "FA_BF16", "FA_FP32"]
+           "lse_merge", "fwd_window", "bwd_window", "FAError", "LibraryNotBuilt", "load_library", "FA_BF16", "FA_FP32"]

@@ -40,6 +40,8 @@ EXPORTS = (
     "fa_fwd_split_workspace_size",
     "fa_fwd_split",
     "fa_lse_merge",
+    "fa_fwd_window",
+    "fa_bwd_window",
 )
 
 
@@ -93,6 +95,10 @@ def load():
     lib.fa_fwd_split.restype = _i
     lib.fa_lse_merge.argtypes = [_vp, _vp, _i, ctypes.c_longlong, _i, _vp, _vp, _i, _vp]
     lib.fa_lse_merge.restype = _i
+    lib.fa_fwd_window.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp]
+    lib.fa_fwd_window.restype = _i
+    lib.fa_bwd_window.argtypes = [_vp] * 10 + [ctypes.c_size_t, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp]
+    lib.fa_bwd_window.restype = _i
     _lib = lib
     return lib
 

@@ -159,3 +159,43 @@ def lse_merge(o_parts, lse_parts, dtype=torch.bfloat16, out=None, lse=None):
     )
     _lib.check(st, "fa_lse_merge")
     return o, lse
+
+
+def fwd_window(q, k, v, window, scale=None, out=None, lse=None):
+    """Local-attention forward: query i sees keys i - window[0] .. i + window[1]
+    (-1: unbounded on that side).  Returns (o, lse) as ``fwd``."""
+    B, Hq, Hkv, N, d = _check(q, k, v)
+    left, right = (int(x) for x in window)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    st = _lib.load().fa_fwd_window(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        lse.data_ptr() or None, B, Hq, Hkv, N, d, float(scale), left, right, _DTYPES[q.dtype], _stream(q.device),
+    )
+    _lib.check(st, "fa_fwd_window")
+    return o, lse
+
+
+def bwd_window(q, k, v, o, lse, do, window, scale=None, workspace=None):
+    """Backward of ``fwd_window`` with the same window: returns (dq, dk, dv)."""
+    B, Hq, Hkv, N, d = _check(q, k, v, o, do)
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H_q, N]")
+    left, right = (int(x) for x in window)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    st = _lib.load().fa_bwd_window(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        do.data_ptr() or None, lse.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,
+        dv.data_ptr() or None, workspace.data_ptr() or None, workspace.numel(),
+        B, Hq, Hkv, N, d, float(scale), left, right, _DTYPES[q.dtype], _stream(q.device),
+    )
+    _lib.check(st, "fa_bwd_window")
+    return dq, dk, dv

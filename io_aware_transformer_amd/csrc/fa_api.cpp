@@ -55,41 +55,20 @@ int split_parts(int B, int Hq, int Hkv, int Nq, int Nk, int d, int splits) {
     return splits > 0 ? splits : fa::split_parts_default(B, Hq, Hkv, Nq, Nk, d);
 }
 
-bool split_grid_ok(int B, int Hq, int Hkv, int Nq, int parts) {
-    const long long rows = (long long)(Hq / Hkv) * Nq;
-    const long long blocks = (long long)B * Hkv * ((rows + 31) / 32) * parts;  // at one wave per workgroup
-    const long long merge_rows = (long long)B * Hq * Nq;
-    return blocks <= (long long)INT_MAX && merge_rows <= (long long)INT_MAX * 4;
-}
-
-}  // namespace
-
-extern "C" {
-
-int fa_version(void) { return 110; }
-
-const char* fa_status_str(int status) {
-    switch (status) {
-        case FA_OK: return "FA_OK";
-        case FA_ERR_NULL: return "FA_ERR_NULL";
-        case FA_ERR_SHAPE: return "FA_ERR_SHAPE";
-        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM";
-        case FA_ERR_DTYPE: return "FA_ERR_DTYPE";
-        case FA_ERR_ALIGN: return "FA_ERR_ALIGN";
-        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
-        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
-        case FA_ERR_HIP: return "FA_ERR_HIP";
-        case FA_ERR_ARG: return "FA_ERR_ARG";
-        default: return "FA_ERR_UNKNOWN";
+// Window bounds -> kernel form.  -1: unbounded; -2: no mask at all (the
+// unmasked kernels).  Returns whether the masked kernels are needed.
+bool window_bounds(int left, int right, int& wl, int& wr) {
+    if (left == -2 && right == -2) {
+        wl = wr = fa::kUnbounded;
+        return false;
     }
+    wl = left < 0 ? fa::kUnbounded : left;
+    wr = right < 0 ? fa::kUnbounded : right;
+    return !(left < 0 && right < 0);  // (-1, -1) is no mask
 }
 
-int fa_last_hip_error(void) { return g_last_hip_error; }
-
-int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N, int d,
-           float scale, int causal, int dtype, void* stream) {
-    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
-    if (st != FA_OK) return st;
+int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N, int d,
+             float scale, int left, int right, int dtype, void* stream) {
     if (B == 0 || N == 0) return FA_OK;
     if (!Q || !K || !V || !O) return FA_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 16))
@@ -105,23 +84,16 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
     p.Hkv = H_kv;
     p.N = N;
     p.scale_log2 = scale * kLog2e;
+    const bool masked = window_bounds(left, right, p.wl, p.wr);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = (dtype == FA_BF16) ? fa::launch_fwd_bf16(p, d, causal, s) : fa::launch_fwd_f32(p, d, causal, s);
+    hipError_t e = (dtype == FA_BF16) ? fa::launch_fwd_bf16(p, d, masked, s) : fa::launch_fwd_f32(p, d, masked, s);
     if (e != hipSuccess) return hip_failure(e);
     return FA_OK;
 }
 
-size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, int dtype) {
-    if (validate(B, H_q, H_kv, N, d, 1.0f, 0, dtype) != FA_OK) return 0;
-    if (B == 0 || N == 0) return 0;
-    return fa::bwd_workspace_bytes(B, H_q, N);
-}
-
-int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
-           void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d,
-           float scale, int causal, int dtype, void* stream) {
-    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
-    if (st != FA_OK) return st;
+int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+             void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d,
+             float scale, int left, int right, int dtype, void* stream) {
     if (dtype == FA_BF16 && d == 256) return FA_ERR_UNSUPPORTED;
     if (B == 0 || N == 0) return FA_OK;
     if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
@@ -147,11 +119,83 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
     p.N = N;
     p.scale = scale;
     p.scale_log2 = scale * kLog2e;
+    const bool masked = window_bounds(left, right, p.wl, p.wr);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = (dtype == FA_BF16) ? fa::launch_bwd_bf16(p, d, causal, s) : fa::launch_bwd_f32(p, d, causal, s);
+    hipError_t e = (dtype == FA_BF16) ? fa::launch_bwd_bf16(p, d, masked, s) : fa::launch_bwd_f32(p, d, masked, s);
     if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
     if (e != hipSuccess) return hip_failure(e);
     return FA_OK;
+}
+
+bool split_grid_ok(int B, int Hq, int Hkv, int Nq, int parts) {
+    const long long rows = (long long)(Hq / Hkv) * Nq;
+    const long long blocks = (long long)B * Hkv * ((rows + 31) / 32) * parts;  // at one wave per workgroup
+    const long long merge_rows = (long long)B * Hq * Nq;
+    return blocks <= (long long)INT_MAX && merge_rows <= (long long)INT_MAX * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 120; }
+
+const char* fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULL: return "FA_ERR_NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE";
+        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM";
+        case FA_ERR_DTYPE: return "FA_ERR_DTYPE";
+        case FA_ERR_ALIGN: return "FA_ERR_ALIGN";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+        case FA_ERR_ARG: return "FA_ERR_ARG";
+        default: return "FA_ERR_UNKNOWN";
+    }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    return fwd_impl(Q, K, V, O, LSE, B, H_q, H_kv, N, d, scale, causal ? -1 : -2, causal ? 0 : -2, dtype, stream);
+}
+
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N,
+                  int d, float scale, int window_left, int window_right, int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, 0, dtype);
+    if (st != FA_OK) return st;
+    if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
+    return fwd_impl(Q, K, V, O, LSE, B, H_q, H_kv, N, d, scale, window_left, window_right, dtype, stream);
+}
+
+size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, int dtype) {
+    if (validate(B, H_q, H_kv, N, d, 1.0f, 0, dtype) != FA_OK) return 0;
+    if (B == 0 || N == 0) return 0;
+    return fa::bwd_workspace_bytes(B, H_q, N);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+           void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H_q, H_kv, N, d, scale,
+                    causal ? -1 : -2, causal ? 0 : -2, dtype, stream);
+}
+
+int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                  void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv,
+                  int N, int d, float scale, int window_left, int window_right, int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, 0, dtype);
+    if (st != FA_OK) return st;
+    if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
+    return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H_q, H_kv, N, d, scale,
+                    window_left, window_right, dtype, stream);
 }
 
 size_t fa_fwd_split_workspace_size(int B, int H_q, int H_kv, int N_q, int N_k, int d, int num_splits, int dtype) {

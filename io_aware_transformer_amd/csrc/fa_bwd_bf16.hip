@@ -14,17 +14,20 @@
 //   2. bwd_dkdv: one workgroup per (batch, kv head, block of keys); each
 //      wave keeps its keys' K and V rows in registers and its dK, dV
 //      accumulators in registers, and walks every query tile (of every
-//      query head of the group) that can see its keys (v2: two 32-key
-//      blocks per wave at d = 64; v3: software-pipelined, d = 128).  S = Q K^T and
+//      query head of the group) that can see its keys.  S = Q K^T and
 //      dP = dO V^T come out with one key per lane, which is exactly the MFMA
 //      A layout of P^T and dS^T, so dV += P^T dO and dK += dS^T Q take the
 //      score registers directly; dO and Q enter as B operands through
 //      transposing LDS reads.  dK, dV are written once: no atomics.
-//   3. bwd_dq:   one workgroup per (batch, query head, 128 queries), the
-//      same shape as the forward: S^T = K Q^T, dP^T = V dO^T with one query
-//      per lane, dQ^T += K^T dS^T with K^T through transposing LDS reads.
+//      v2 keeps two 32-key blocks per wave (d = 64); v3 is software-
+//      pipelined with one block per wave (d = 128).
+//   3. bwd_dq:   one workgroup per (batch, query head, 256 queries), 64 rows
+//      per wave: S^T = K Q^T, dP^T = V dO^T with one query per lane,
+//      dQ^T += K^T dS^T with K^T through transposing LDS reads.
 // Splitting dQ from dK/dV recomputes S and dP once more (7 matrix products
 // instead of 5) but needs no fp32 dQ accumulator and no atomic traffic.
+// The masked kernels (MASK 1: causal, 2: a window (wl, wr)) visit only the
+// tiles a window can see and mask the scores of the edge tiles.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -32,9 +35,6 @@
 
 #include <type_traits>
 
-#ifndef FA_BWD_DKDV_V1
-#define FA_BWD_DKDV_V1 0
-#endif
 #ifndef FA_BWD_DKDV3
 #define FA_BWD_DKDV3 1
 #endif
@@ -76,212 +76,6 @@ __device__ __forceinline__ int remap_unit(int u, int units) {
     return (units % 8 == 0) ? (u & 7) * (units >> 3) + (u >> 3) : u;
 }
 
-// ---------------------------------------------------------------- bwd_dkdv
-constexpr int kKB = 128;  // keys per workgroup (32 per wave)
-constexpr int kBQ = 64;   // query rows per staged tile
-
-template <int D>
-constexpr size_t dkdv_stage_bytes() {
-    return size_t(2) * kBQ * D * sizeof(bf16) + 2 * kBQ * sizeof(float);
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
-    constexpr int CPR = D / 8;
-    constexpr int QT = kBQ * D;
-    constexpr int NLD = kBQ * CPR / 256;
-    static_assert(NLD >= 1 && (kBQ * CPR) % 256 == 0, "tile must split evenly over 256 threads");
-    constexpr int STAGE = int(dkdv_stage_bytes<D>());
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int N = p.N;
-    const int units = p.B * p.Hkv;
-    const int slot = blockIdx.x / units;
-    const int unit = remap_unit(blockIdx.x - slot * units, units);
-    const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
-    const int G = p.Hq / p.Hkv;
-    const int kstart = slot * kKB;  // causal: small kstart = most query tiles = issued first
-    const int kw0 = kstart + 32 * w;
-    const int key = kw0 + l32;
-
-    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
-    const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
-    const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
-
-    // K and V rows of this lane's key as MFMA B operands (8 dims per lane).
-    bf16x8 kreg[D / 16], vreg[D / 16];
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-        if (key < N) {
-            kreg[c] = as_bf16x8(ld16(Kh + size_t(key) * D + 16 * c + 8 * hi));
-            vreg[c] = as_bf16x8(ld16(Vh + size_t(key) * D + 16 * c + 8 * hi));
-        } else {
-            kreg[c] = bf16x8{};
-            vreg[c] = bf16x8{};
-        }
-    }
-    f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        dk[db] = f32x16{};
-        dv[db] = f32x16{};
-    }
-
-    const int nqt = (N + kBQ - 1) / kBQ;
-    const int qt_first = CAUSAL ? kstart / kBQ : 0;
-    const int per_head = nqt - qt_first;
-    const int iters = G * per_head;
-
-    u32x4 qpre[NLD], opre[NLD];
-    float lpre = 0.f, dpre = 0.f;
-    auto gload = [&](int t) {
-        const int hq = g * G + t / per_head;
-        const int q0 = (qt_first + t % per_head) * kBQ;
-        const size_t qoff = size_t(b * p.Hq + hq) * size_t(N);
-        const bf16* Qh = static_cast<const bf16*>(p.Q) + qoff * D;
-        const bf16* dOh = static_cast<const bf16*>(p.dO) + qoff * D;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / CPR, c = idx % CPR;
-            const int q = q0 + r;
-            if (q < N) {
-                qpre[i] = ld16(Qh + size_t(q) * D + 8 * c);
-                opre[i] = ld16(dOh + size_t(q) * D + 8 * c);
-            } else {
-                qpre[i] = u32x4{0, 0, 0, 0};
-                opre[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-        if (tid < kBQ) {
-            const int q = q0 + tid;
-            // rows past N get LSE = +inf so that their P is exactly 0
-            lpre = (q < N) ? p.LSE[qoff + q] * kLog2e : INFINITY;
-            dpre = (q < N) ? p.Drow[qoff + q] : 0.f;
-        }
-    };
-    auto lstore = [&](int stage) {
-        unsigned char* base = smem_raw + stage * STAGE;
-        bf16* Qs = reinterpret_cast<bf16*>(base);
-        bf16* dOs = Qs + QT;
-        float* ls = reinterpret_cast<float*>(dOs + QT);
-        float* ds = ls + kBQ;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / CPR, c = idx % CPR;
-            st16(Qs + r * D + 8 * swz_both<D>(r, c), qpre[i]);
-            st16(dOs + r * D + 8 * swz_both<D>(r, c), opre[i]);
-        }
-        if (tid < kBQ) {
-            ls[tid] = lpre;
-            ds[tid] = dpre;
-        }
-    };
-
-    const int trow = 4 * hi + ((lane & 15) >> 2);
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-    if (iters > 0 && kstart < N) {
-        gload(0);
-        lstore(0);
-    }
-    __syncthreads();
-    for (int t = 0; t < iters && kstart < N; ++t) {
-        const int stage = t & 1;
-        if (t + 1 < iters) gload(t + 1);
-        const unsigned char* base = smem_raw + stage * STAGE;
-        const bf16* Qs = reinterpret_cast<const bf16*>(base);
-        const bf16* dOs = Qs + QT;
-        const float* ls = reinterpret_cast<const float*>(dOs + QT);
-        const float* dsr = ls + kBQ;
-        const int q0 = (qt_first + t % per_head) * kBQ;
-
-#pragma unroll
-        for (int qs = 0; qs < kBQ / 32; ++qs) {
-            const int qb0 = q0 + 32 * qs;
-            if (CAUSAL && qb0 + 31 < kw0) continue;  // every query precedes every key of this wave
-            if (qb0 >= N) continue;
-            // S = Q K^T and dP = dO V^T: lane = key, register r = query qb0 + 8(r/4) + 4hi + r%4
-            f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 aq = as_bf16x8(ld16(Qs + off_both<D>(32 * qs + l32, 16 * c + 8 * hi)));
-                s = mfma_32x32x16(aq, kreg[c], s);
-            }
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 ao = as_bf16x8(ld16(dOs + off_both<D>(32 * qs + l32, 16 * c + 8 * hi)));
-                dp = mfma_32x32x16(ao, vreg[c], dp);
-            }
-            float lq[16], dq[16];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 lv = *reinterpret_cast<const f32x4*>(ls + 32 * qs + 8 * j + 4 * hi);
-                const f32x4 dv4 = *reinterpret_cast<const f32x4*>(dsr + 32 * qs + 8 * j + 4 * hi);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lq[4 * j + e] = lv[e];
-                    dq[4 * j + e] = dv4[e];
-                }
-            }
-            const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (kw0 + 31 >= N);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float pr = fast_exp2(s[r] * p.scale_log2 - lq[r]);
-                if (need_mask) {
-                    const int q = qb0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if ((CAUSAL && key > q) || key >= N) pr = 0.f;
-                }
-                s[r] = pr;
-                dp[r] = pr * (dp[r] - dq[r]);
-            }
-            bf16x8 pb[2], sb[2];
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                pb[cc] = to_bf16x8(s[8 * cc + 0], s[8 * cc + 1], s[8 * cc + 2], s[8 * cc + 3], s[8 * cc + 4],
-                                   s[8 * cc + 5], s[8 * cc + 6], s[8 * cc + 7]);
-                sb[cc] = to_bf16x8(dp[8 * cc + 0], dp[8 * cc + 1], dp[8 * cc + 2], dp[8 * cc + 3], dp[8 * cc + 4],
-                                   dp[8 * cc + 5], dp[8 * cc + 6], dp[8 * cc + 7]);
-            }
-            // dV += P^T dO, dK += dS^T Q.  Contraction slot (cc, hi, sl) <-> query
-            // 32qs + 16cc + 8(sl/4) + 4hi + sl%4 on both operands.
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int qr = 32 * qs + 16 * cc + trow;
-                    const bf16x4 o0 = lds_read_tr(dOs + off_both<D>(qr, db * 32 + tcol));
-                    const bf16x4 o1 = lds_read_tr(dOs + off_both<D>(qr + 8, db * 32 + tcol));
-                    dv[db] = mfma_32x32x16(pb[cc], cat(o0, o1), dv[db]);
-                    const bf16x4 q0v = lds_read_tr(Qs + off_both<D>(qr, db * 32 + tcol));
-                    const bf16x4 q1v = lds_read_tr(Qs + off_both<D>(qr + 8, db * 32 + tcol));
-                    dk[db] = mfma_32x32x16(sb[cc], cat(q0v, q1v), dk[db]);
-                }
-            }
-        }
-        if (t + 1 < iters) lstore(stage ^ 1);
-        __syncthreads();
-    }
-
-    // Epilogue: lane holds dim db*32 + l32 of keys kw0 + 8(r/4) + 4hi + r%4.
-    bf16* dKh = static_cast<bf16*>(p.dK) + kvoff;
-    bf16* dVh = static_cast<bf16*>(p.dV) + kvoff;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kk = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (kk < N) {
-                dKh[size_t(kk) * D + db * 32 + l32] = (bf16)(dk[db][r] * p.scale);
-                dVh[size_t(kk) * D + db * 32 + l32] = (bf16)(dv[db][r]);
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------- bwd_dkdv v2
 // One workgroup of 4 waves per (batch, kv head, block of 32*KPW*4 keys); each
 // wave keeps KPW blocks of 32 keys (K and V rows as MFMA B operands) and
@@ -321,9 +115,15 @@ constexpr int dk_keys_per_wg() {
     return 32 * DkCfg<D>::KPW * kDkWaves;
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ __launch_bounds__(kDkWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv2_kernel(BwdParams p) {
+    // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
+    // time); 2: the window (p.wl, p.wr).
+    constexpr bool CAUSAL = MASK != 0;
+    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
+    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
+    const int wr_ = MASK == 2 ? p.wr : 0;
     constexpr int KPW = DkCfg<D>::KPW;
     using QL = typename DkLds<D>::QL;
     constexpr int TB = DkLds<D>::TILE_BYTES;
@@ -373,9 +173,12 @@ void bwd_dkdv2_kernel(BwdParams p) {
         }
     }
 
+    // Query tiles that can see a key of this workgroup: queries k - wr .. k + wl
+    // of each key k (masked kernels; causal: wr = 0, wl unbounded).
     const int nqt = (N + BQ - 1) / BQ;
-    const int qt_first = CAUSAL ? kstart / BQ : 0;
-    const int per_head = nqt - qt_first;
+    const int qt_first = CAUSAL ? max(0, kstart - wr_) / BQ : 0;
+    const int qt_last = WIN ? min(nqt - 1, (kstart + dk_keys_per_wg<D>() - 1 + wl_) / BQ) : nqt - 1;
+    const int per_head = qt_last - qt_first + 1;
     const int iters = G * per_head;
 
     // Per-lane copy sources: piece pi = w + 4 i of the Q (and dO) tile.
@@ -437,10 +240,17 @@ void bwd_dkdv2_kernel(BwdParams p) {
 #pragma unroll
         for (int qs = 0; qs < BQ / 32; ++qs) {
             const int qb0 = q0 + 32 * qs;
-            bool act[KPW];
+            // Skip the subtile when no key block of this wave sees any of its
+            // rows; otherwise compute every block (a block that sees none is
+            // wholly hidden by the mask below and adds zeros), which keeps the
+            // matrix-core code free of branches.
+            bool any = false;
 #pragma unroll
-            for (int kb = 0; kb < KPW; ++kb) act[kb] = (!CAUSAL || qb0 + 31 >= kw0 + 32 * kb) && qb0 < N;
-            if (!act[0]) continue;  // block 0 has the smallest keys
+            for (int kb = 0; kb < KPW; ++kb) {
+                const int key0 = kw0 + 32 * kb;
+                any = any || ((!CAUSAL || (qb0 + 31 >= key0 - wr_ && (!WIN || qb0 <= key0 + 31 + wl_))) && qb0 < N);
+            }
+            if (!any) continue;
             // S = Q K^T, dP = dO V^T: lane = key, register r = query qb0 + 8(r/4) + 4hi + r%4
             f32x16 sacc[KPW], dpacc[KPW];
 #pragma unroll
@@ -451,7 +261,6 @@ void bwd_dkdv2_kernel(BwdParams p) {
                 const bf16x8 ao = as_bf16x8(ld16(dOs + QL::off(32 * qs + l32, 16 * cc + 8 * hi)));
 #pragma unroll
                 for (int kb = 0; kb < KPW; ++kb) {
-                    if (!act[kb]) continue;
                     sacc[kb] = mfma_32x32x16(aq, kreg[kb][cc], sacc[kb]);
                     dpacc[kb] = mfma_32x32x16(ao, vreg[kb][cc], dpacc[kb]);
                 }
@@ -477,14 +286,15 @@ void bwd_dkdv2_kernel(BwdParams p) {
                     ds[r] = pr[r] * (dpacc[kb][r] - dq[r]);
                 }
                 const int key0 = kw0 + 32 * kb;
-                if ((CAUSAL && qb0 < key0 + 31) || qb0 + 31 >= N) {
-                    // hide q < key (causal) and rows q >= N: both P and dS become 0
-                    const int thr = CAUSAL ? key0 + l32 - qb0 - 4 * hi : -1;
+                if ((CAUSAL && (qb0 < key0 + 31 - wr_ || (WIN && qb0 + 31 > key0 + wl_))) || qb0 + 31 >= N) {
+                    // hide queries outside key - wr .. key + wl and rows q >= N: P and dS become 0
+                    const int thr = CAUSAL ? key0 + l32 - wr_ - qb0 - 4 * hi : -1;
+                    const int thr_hi = WIN ? key0 + l32 + wl_ - qb0 - 4 * hi : kUnbounded;
                     const int nlim = N - qb0 - 4 * hi;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int qo = 8 * (r >> 2) + (r & 3);
-                        const bool hide = (qo < thr) || (qo >= nlim);
+                        const bool hide = (qo < thr) || (qo > thr_hi) || (qo >= nlim);
                         pr[r] = hide ? 0.f : pr[r];
                         ds[r] = hide ? 0.f : ds[r];
                     }
@@ -510,7 +320,6 @@ void bwd_dkdv2_kernel(BwdParams p) {
                                           lds_read_tr(Qs + QL::off(qr + 8, db * 32 + tcol)));
 #pragma unroll
                     for (int kb = 0; kb < KPW; ++kb) {
-                        if (!act[kb]) continue;
                         dv[kb][db] = mfma_32x32x16(pb[kb][cc], bo, dv[kb][db]);
                         dk[kb][db] = mfma_32x32x16(sb[kb][cc], bq, dk[kb][db]);
                     }
@@ -567,9 +376,15 @@ struct Dk3Lds {
 };
 constexpr int kDk3KeysPerWg = 32 * kDkWaves;
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ __launch_bounds__(kDkWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv3_kernel(BwdParams p) {
+    // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
+    // time); 2: the window (p.wl, p.wr).
+    constexpr bool CAUSAL = MASK != 0;
+    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
+    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
+    const int wr_ = MASK == 2 ? p.wr : 0;
     using QL = typename Dk3Lds<D>::QL;
     constexpr int TB = Dk3Lds<D>::TILE_BYTES;
     constexpr int SB = Dk3Lds<D>::STAGE_BYTES;
@@ -616,9 +431,12 @@ void bwd_dkdv3_kernel(BwdParams p) {
         for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
     }
 
+    // Query tiles that can see a key of this workgroup (masked kernels: the
+    // queries k - wr .. k + wl of each key k).
     const int nqt = (N + BQ - 1) / BQ;
-    const int qt_first = CAUSAL ? kstart / BQ : 0;
-    const int per_head = nqt - qt_first;
+    const int qt_first = CAUSAL ? max(0, kstart - wr_) / BQ : 0;
+    const int qt_last = WIN ? min(nqt - 1, (kstart + kDk3KeysPerWg - 1 + wl_) / BQ) : nqt - 1;
+    const int per_head = qt_last - qt_first + 1;
     const int iters = G * per_head;  // >= 1
 
     int src_off[PPW];
@@ -711,7 +529,7 @@ void bwd_dkdv3_kernel(BwdParams p) {
     };
     auto needs_mask = [&](int i) {
         const int qb0 = tile_q0(i >> 1) + 32 * (i & 1);
-        return (CAUSAL && qb0 < kw0 + 31) || qb0 + 31 >= N;
+        return (CAUSAL && (qb0 < kw0 + 31 - wr_ || (WIN && qb0 + 31 > kw0 + wl_))) || qb0 + 31 >= N;
     };
     constexpr int RPC = 16 / NC;       // score rows (registers) of B per slot
     constexpr int TPC = 8 * NDB / NC;  // transposing reads per slot
@@ -723,8 +541,9 @@ void bwd_dkdv3_kernel(BwdParams p) {
     auto step1 = [&](int i, const f32x16& s_cur, const f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt,
                      bool has_next, auto masked) {
         const int qb0 = tile_q0(i >> 1) + 32 * (i & 1);
-        const int thr = CAUSAL ? kw0 + l32 - qb0 - 4 * hi : -1 - 4 * hi;
-        const int nlim = N - qb0 - 4 * hi;
+        const int thr = CAUSAL ? kw0 + l32 - wr_ - qb0 - 4 * hi : -1 - 4 * hi;     // q < key - wr
+        const int thr_hi = WIN ? kw0 + l32 + wl_ - qb0 - 4 * hi : kUnbounded;  // q > key + wl
+        const int nlim = N - qb0 - 4 * hi;                                          // q >= N
         if (has_next) s_nxt = dp_nxt = f32x16{};
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
@@ -739,7 +558,7 @@ void bwd_dkdv3_kernel(BwdParams p) {
                 float ex = fmaf(s_cur[r], c, -lq4[r >> 2][r & 3] * kLog2e);
                 if constexpr (decltype(masked)::value) {
                     const int qo = 8 * (r >> 2) + (r & 3);
-                    ex = (qo < thr || qo >= nlim) ? -INFINITY : ex;
+                    ex = (qo < thr || qo > thr_hi || qo >= nlim) ? -INFINITY : ex;
                 }
                 pr[r] = fast_exp2(ex);
                 ds[r] = pr[r] * (dp_cur[r] - dd4[r >> 2][r & 3]);
@@ -840,161 +659,6 @@ void bwd_dkdv3_kernel(BwdParams p) {
     }
 }
 
-// ---------------------------------------------------------------- bwd_dq
-constexpr int kQB = 128;  // query rows per workgroup (32 per wave)
-constexpr int kBNdq = 64;  // keys per staged tile
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
-    constexpr int CPR = D / 8;
-    constexpr int TILE = kBNdq * D;
-    constexpr int NLD = kBNdq * CPR / 256;
-    static_assert(NLD >= 1 && (kBNdq * CPR) % 256 == 0, "tile must split evenly over 256 threads");
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    bf16* smem = reinterpret_cast<bf16*>(smem_raw);
-
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int N = p.N;
-    const int units = p.B * p.Hq;
-    const int slot = blockIdx.x / units;
-    const int unit = remap_unit(blockIdx.x - slot * units, units);
-    const int qb = CAUSAL ? p.nqb - 1 - slot : slot;
-    const int b = unit / p.Hq, h = unit - (unit / p.Hq) * p.Hq;
-    const int g = h / (p.Hq / p.Hkv);
-    const size_t qrows = size_t(b * p.Hq + h) * size_t(N);
-    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
-    const bf16* __restrict__ Qh = static_cast<const bf16*>(p.Q) + qrows * D;
-    const bf16* __restrict__ dOh = static_cast<const bf16*>(p.dO) + qrows * D;
-    const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
-    const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
-
-    const int q0 = qb * kQB;
-    const int wq0 = q0 + 32 * w;
-    const int qrow = wq0 + l32;
-
-    bf16x8 qreg[D / 16], oreg[D / 16];
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-        if (qrow < N) {
-            qreg[c] = as_bf16x8(ld16(Qh + size_t(qrow) * D + 16 * c + 8 * hi));
-            oreg[c] = as_bf16x8(ld16(dOh + size_t(qrow) * D + 16 * c + 8 * hi));
-        } else {
-            qreg[c] = bf16x8{};
-            oreg[c] = bf16x8{};
-        }
-    }
-    const float lse2 = (qrow < N) ? p.LSE[qrows + qrow] * kLog2e : INFINITY;
-    const float drow = (qrow < N) ? p.Drow[qrows + qrow] : 0.f;
-
-    const int kend = CAUSAL ? min(N, q0 + kQB) : N;
-    const int ntiles = (kend + kBNdq - 1) / kBNdq;
-
-    u32x4 kpre[NLD], vpre[NLD];
-    auto gload = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / CPR, c = idx % CPR;
-            const int kk = kt * kBNdq + r;
-            if (kk < N) {
-                kpre[i] = ld16(Kh + size_t(kk) * D + 8 * c);
-                vpre[i] = ld16(Vh + size_t(kk) * D + 8 * c);
-            } else {
-                kpre[i] = u32x4{0, 0, 0, 0};
-                vpre[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto lstore = [&](int stage) {
-        bf16* Ks = smem + stage * 2 * TILE;
-        bf16* Vs = Ks + TILE;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / CPR, c = idx % CPR;
-            st16(Ks + r * D + 8 * swz_both<D>(r, c), kpre[i]);
-            st16(Vs + r * D + 8 * swz_row<D>(r, c), vpre[i]);
-        }
-    };
-
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-    const int trow = 4 * hi + ((lane & 15) >> 2);
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int stage = kt & 1;
-        if (kt + 1 < ntiles) gload(kt + 1);
-        const bf16* Ks = smem + stage * 2 * TILE;
-        const bf16* Vs = Ks + TILE;
-        const int kstart = kt * kBNdq;
-#pragma unroll
-        for (int kb = 0; kb < kBNdq / 32; ++kb) {
-            const int kb0 = kstart + 32 * kb;
-            if (CAUSAL && kb0 > wq0 + 31) continue;  // every key follows every query of this wave
-            if (kb0 >= N) continue;
-            // S^T = K Q^T, dP^T = V dO^T: lane = query, register r = key kb0 + 8(r/4) + 4hi + r%4
-            f32x16 s = f32x16{}, dpt = f32x16{};
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 ak = as_bf16x8(ld16(Ks + off_both<D>(32 * kb + l32, 16 * c + 8 * hi)));
-                s = mfma_32x32x16(ak, qreg[c], s);
-            }
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 av = as_bf16x8(ld16(Vs + off_row<D>(32 * kb + l32, 16 * c + 8 * hi)));
-                dpt = mfma_32x32x16(av, oreg[c], dpt);
-            }
-            const bool need_mask = (CAUSAL && kb0 + 31 > wq0) || (kb0 + 31 >= N);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float pr = fast_exp2(s[r] * p.scale_log2 - lse2);
-                if (need_mask) {
-                    const int kk = kb0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if ((CAUSAL && kk > qrow) || kk >= N) pr = 0.f;
-                }
-                s[r] = pr * (dpt[r] - drow);
-            }
-            bf16x8 sb[2];
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
-                sb[cc] = to_bf16x8(s[8 * cc + 0], s[8 * cc + 1], s[8 * cc + 2], s[8 * cc + 3], s[8 * cc + 4],
-                                   s[8 * cc + 5], s[8 * cc + 6], s[8 * cc + 7]);
-            // dQ^T += K^T dS^T
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int kr = 32 * kb + 16 * cc + trow;
-                    const bf16x4 k0 = lds_read_tr(Ks + off_both<D>(kr, db * 32 + tcol));
-                    const bf16x4 k1 = lds_read_tr(Ks + off_both<D>(kr + 8, db * 32 + tcol));
-                    acc[db] = mfma_32x32x16(cat(k0, k1), sb[cc], acc[db]);
-                }
-            }
-        }
-        if (kt + 1 < ntiles) lstore(stage ^ 1);
-        __syncthreads();
-    }
-
-    if (qrow < N) {
-        bf16* dQh = static_cast<bf16*>(p.dQ) + qrows * D + size_t(qrow) * D;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x4 v = bf16x4{(bf16)(acc[db][4 * j + 0] * p.scale), (bf16)(acc[db][4 * j + 1] * p.scale),
-                                        (bf16)(acc[db][4 * j + 2] * p.scale), (bf16)(acc[db][4 * j + 3] * p.scale)};
-                *reinterpret_cast<bf16x4*>(dQh + db * 32 + 8 * j + 4 * hi) = v;
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------- bwd_dq v2
 // One workgroup of 4 waves per (batch, query head, 256 queries); each wave
 // owns two 32-row blocks (Q and dO rows as B operands, dQ accumulators), so
@@ -1014,9 +678,15 @@ struct DqLds {
     static constexpr size_t BYTES = size_t(kDqStages) * STAGE_BYTES;
 };
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ __launch_bounds__(kDqWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq2_kernel(BwdParams p) {
+    // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
+    // time); 2: the window (p.wl, p.wr).
+    constexpr bool CAUSAL = MASK != 0;
+    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
+    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
+    const int wr_ = MASK == 2 ? p.wr : 0;
     using KL = typename DqLds<D>::KL;
     constexpr int TB = DqLds<D>::TILE_BYTES;
     constexpr int SB = DqLds<D>::STAGE_BYTES;
@@ -1050,7 +720,7 @@ void bwd_dq2_kernel(BwdParams p) {
 
     bf16x8 qreg[2][D / 16], oreg[2][D / 16];
     float lse2[2], drow[2];
-    int key_lim[2];
+    int key_lim[2], key_lo[2];  // visible keys of each row block's lane: key_lo .. key_lim
     f32x16 acc[2][D / 32];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -1068,13 +738,16 @@ void bwd_dq2_kernel(BwdParams p) {
         // rows past N: LSE = +inf makes P exactly 0
         lse2[rb] = (qrow < N) ? p.LSE[qrows + qrow] * kLog2e : INFINITY;
         drow[rb] = (qrow < N) ? p.Drow[qrows + qrow] : 0.f;
-        key_lim[rb] = CAUSAL ? min(qrow, N - 1) : N - 1;
+        key_lim[rb] = CAUSAL ? min(qrow + wr_, N - 1) : N - 1;
+        key_lo[rb] = WIN ? qrow - wl_ : 0;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[rb][db] = f32x16{};
     }
 
-    const int kend = CAUSAL ? min(N, q0 + kDqBM) : N;
-    const int ntiles = (kend + BN - 1) / BN;
+    // Key tiles [kt0, kt0 + ntiles): masked kernels see keys q - wl .. q + wr.
+    const int kend = CAUSAL ? min(N, q0 + kDqBM + wr_) : N;
+    const int kt0 = WIN ? max(0, q0 - wl_) / BN : 0;
+    const int ntiles = (kend + BN - 1) / BN - kt0;
 
     int src_off[PPW];
 #pragma unroll
@@ -1084,7 +757,7 @@ void bwd_dq2_kernel(BwdParams p) {
         src_off[i] = r * D + e0;
     }
     auto issue = [&](int kt) {
-        const int key0 = kt * BN;
+        const int key0 = (kt0 + kt) * BN;
         unsigned char* st = smem_raw + (kt % NST) * SB;
         const uint32_t bytes = uint32_t(N - key0) * uint32_t(D * 2);
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kh + size_t(key0) * D, bytes);
@@ -1113,11 +786,11 @@ void bwd_dq2_kernel(BwdParams p) {
         if (more) issue(kt + 2);
         const bf16* Ks = reinterpret_cast<const bf16*>(smem_raw + (kt % NST) * SB);
         const bf16* Vs = reinterpret_cast<const bf16*>(smem_raw + (kt % NST) * SB + TB);
-        const int kstart = kt * BN;
+        const int kstart = (kt0 + kt) * BN;
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
             const int kb0 = kstart + 32 * kb;
-            if ((CAUSAL && kb0 > wq_last) || kb0 >= N) continue;
+            if ((CAUSAL && (kb0 > wq_last + wr_ || (WIN && kb0 + 31 < wq0 - wl_))) || kb0 >= N) continue;
             // S^T = K Q^T, dP^T = V dO^T for both row blocks: lane = query,
             // register r = key kb0 + 8(r/4) + 4hi + r%4
             f32x16 s[2], dpt[2];
@@ -1141,10 +814,15 @@ void bwd_dq2_kernel(BwdParams p) {
                     const float pr = fast_exp2(fmaf(s[rb][r], c, -lse2[rb]));
                     ds[r] = pr * (dpt[rb][r] - drow[rb]);
                 }
-                if ((CAUSAL && kb0 + 31 > wq0 + 32 * rb) || kb0 + 31 >= N) {
+                if ((CAUSAL && (kb0 + 31 > wq0 + 32 * rb + wr_ || (WIN && kb0 < wq0 + 32 * rb + 31 - wl_))) ||
+                    kb0 + 31 >= N) {
                     const int lim = key_lim[rb] - kb0 - 4 * hi;
+                    const int lo = key_lo[rb] - kb0 - 4 * hi;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) ds[r] = (8 * (r >> 2) + (r & 3) > lim) ? 0.f : ds[r];
+                    for (int r = 0; r < 16; ++r) {
+                        const int kk = 8 * (r >> 2) + (r & 3);
+                        ds[r] = (kk > lim || (WIN && kk < lo)) ? 0.f : ds[r];
+                    }
                 }
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc)
@@ -1197,7 +875,7 @@ hipError_t set_lds(K kern, size_t bytes, bool& done) {
     return e;
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     // 1. D_i = dO_i . O_i
     const long long rows = (long long)p.B * p.Hq * p.N;
@@ -1208,20 +886,8 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     if (e != hipSuccess) return e;
 
     // 2. dK, dV
-#if FA_BWD_DKDV_V1
-    {
-        auto kern = bwd_dkdv_kernel<D, CAUSAL>;
-        constexpr size_t lds = 2 * dkdv_stage_bytes<D>();
-        static bool attr = false;
-        if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
-        p.nkb = (p.N + kKB - 1) / kKB;
-        const long long blocks = (long long)p.nkb * p.B * p.Hkv;
-        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), lds, stream, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-#else
     if (FA_BWD_DKDV3 && (D == 128 || FA_BWD_DKDV3_D64)) {
-        auto kern = bwd_dkdv3_kernel<D, CAUSAL>;
+        auto kern = bwd_dkdv3_kernel<D, MASK>;
         constexpr size_t lds = Dk3Lds<D>::BYTES;
         static bool attr = false;
         if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
@@ -1230,7 +896,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
-        auto kern = bwd_dkdv2_kernel<D, CAUSAL>;
+        auto kern = bwd_dkdv2_kernel<D, MASK>;
         constexpr size_t lds = DkLds<D>::BYTES;
         static bool attr = false;
         if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
@@ -1239,22 +905,9 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-#endif
     // 3. dQ
-#if FA_BWD_DKDV_V1
     {
-        auto kern = bwd_dq_kernel<D, CAUSAL>;
-        constexpr size_t lds = size_t(2) * 2 * kBNdq * D * sizeof(bf16);
-        static bool attr = false;
-        if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
-        p.nqb = (p.N + kQB - 1) / kQB;
-        const long long blocks = (long long)p.nqb * p.B * p.Hq;
-        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256), lds, stream, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-#else
-    {
-        auto kern = bwd_dq2_kernel<D, CAUSAL>;
+        auto kern = bwd_dq2_kernel<D, MASK>;
         constexpr size_t lds = DqLds<D>::BYTES;
         static bool attr = false;
         if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
@@ -1263,16 +916,21 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDqWaves * 64), lds, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-#endif
     return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(BwdParams p, int d, int causal, hipStream_t stream) {
+    // 0: no mask, 1: causal, 2: a general window
+    const int mk = !causal ? 0 : (p.wl >= kUnbounded && p.wr == 0) ? 1 : 2;
     switch (d) {
-        case 64: return causal ? launch_bwd_t<64, true>(p, stream) : launch_bwd_t<64, false>(p, stream);
-        case 128: return causal ? launch_bwd_t<128, true>(p, stream) : launch_bwd_t<128, false>(p, stream);
+        case 64:
+            return mk == 0 ? launch_bwd_t<64, 0>(p, stream)
+                           : mk == 1 ? launch_bwd_t<64, 1>(p, stream) : launch_bwd_t<64, 2>(p, stream);
+        case 128:
+            return mk == 0 ? launch_bwd_t<128, 0>(p, stream)
+                           : mk == 1 ? launch_bwd_t<128, 1>(p, stream) : launch_bwd_t<128, 2>(p, stream);
         default: return hipErrorNotSupported;
     }
 }

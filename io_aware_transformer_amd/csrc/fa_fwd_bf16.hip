@@ -154,9 +154,15 @@ struct TileCopy {
     }
 };
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ __launch_bounds__(FwdCfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE)))
 void fwd_bf16_kernel(FwdParams p) {
+    // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
+    // time); 2: the window (p.wl, p.wr).
+    constexpr bool CAUSAL = MASK != 0;
+    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
+    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
+    const int wr_ = MASK == 2 ? p.wr : 0;
     constexpr int NW = FwdCfg<D>::NW, BN = FwdCfg<D>::BN, NST = FwdCfg<D>::NST;
     constexpr int BM = 32 * NW;
     constexpr int TILE = BN * D;
@@ -185,14 +191,16 @@ void fwd_bf16_kernel(FwdParams p) {
     const int wq_last = wq0 + 31;
     const int qrow = wq0 + l32;   // the query row of this lane
 
-    const int kend = CAUSAL ? min(N, q0 + BM) : N;
-    const int ntiles = (kend + BN - 1) / BN;
+    // Key tiles [kt0, kt0 + ntiles); masked kernels see keys q - wl .. q + wr.
+    const int kend = CAUSAL ? min(N, q0 + BM + wr_) : N;
+    const int kt0 = WIN ? max(0, q0 - wl_) / BN : 0;
+    const int ntiles = (kend + BN - 1) / BN - kt0;
 
     TileCopy<D, BN, NW> cp;
     cp.init(w, lane);
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
-        if (st < ntiles) cp.issue(Kh, Vh, smem + st * 2 * TILE, smem + st * 2 * TILE + TILE, st * BN, N);
+        if (st < ntiles) cp.issue(Kh, Vh, smem + st * 2 * TILE, smem + st * 2 * TILE + TILE, (kt0 + st) * BN, N);
 
     // Q rows of this wave as MFMA B operands: Q[qrow][16cc + 8hi .. +7].
     // qmode 1 negates (negative scale), 2 zeroes (zero scale).
@@ -208,12 +216,13 @@ void fwd_bf16_kernel(FwdParams p) {
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    float m = -INFINITY;  // running (reference) max of c*s
+    float m = -3.0e38f;  // running (reference) max of c*s; finite floor (rows masked in early tiles)
     float l = 0.f;        // running sum over this lane's keys (halves merged at the end)
     const int trow = 4 * hi + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     // Row limit for masking: keys above it are hidden (causal and/or past N).
-    const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+    const int key_lim = CAUSAL ? min(qrow + wr_, N - 1) : N - 1;
+    const int key_lo = WIN ? qrow - wl_ : 0;
 
     wait_vmem();
     __syncthreads();
@@ -223,14 +232,14 @@ void fwd_bf16_kernel(FwdParams p) {
             const int nt = kt + NST - 1;
             if (nt < ntiles) {
                 bf16* st = smem + (nt % NST) * 2 * TILE;
-                cp.issue(Kh, Vh, st, st + TILE, nt * BN, N);
+                cp.issue(Kh, Vh, st, st + TILE, (kt0 + nt) * BN, N);
             }
         }
         const bf16* Ks = smem + (kt % NST) * 2 * TILE;
         const bf16* Vs = Ks + TILE;
-        const int kstart = kt * BN;
+        const int kstart = (kt0 + kt) * BN;
 
-        if (!CAUSAL || kstart <= wq_last) {
+        if (!CAUSAL || (kstart <= wq_last + wr_ && (!WIN || kstart + BN - 1 >= wq0 - wl_))) {
             // S^T blocks: s[kb][r] = score(key kstart + 32kb + 8(r/4) + 4hi + r%4, query qrow).
             // The KB accumulation chains are interleaved so consecutive MFMAs are independent.
             f32x16 s[KB];
@@ -240,19 +249,23 @@ void fwd_bf16_kernel(FwdParams p) {
             for (int cc = 0; cc < D / 16; ++cc) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    if (CAUSAL && kstart + 32 * kb > wq_last) continue;
+                    if (CAUSAL && kstart + 32 * kb > wq_last + wr_) continue;
                     const bf16x8 a = as_bf16x8(ld16(Ks + kslab_off<BN>(kb * 32 + l32, 16 * cc + 8 * hi)));
                     s[kb] = mfma_32x32x16(a, qreg[cc], s[kb]);
                 }
             }
-            const bool need_mask = (CAUSAL && kstart + BN - 1 > wq0) || (kstart + BN > N);
+            const bool need_mask =
+                (CAUSAL && (kstart + BN - 1 > wq0 + wr_ || (WIN && kstart < wq_last - wl_))) || (kstart + BN > N);
             if (need_mask) {
                 const int lim = key_lim - kstart - 4 * hi;
+                const int lo = key_lo - kstart - 4 * hi;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[kb][r];
+                    for (int r = 0; r < 16; ++r) {
+                        const int kk = kb * 32 + 8 * (r >> 2) + (r & 3);
+                        s[kb][r] = (kk > lim || (WIN && kk < lo)) ? -INFINITY : s[kb][r];
+                    }
             }
             float mx = -INFINITY;
 #pragma unroll
@@ -291,7 +304,7 @@ void fwd_bf16_kernel(FwdParams p) {
             // Consecutive MFMAs update different dim blocks (independent accumulators).
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                if (CAUSAL && kstart + 32 * kb > wq_last) continue;
+                if (CAUSAL && kstart + 32 * kb > wq_last + wr_) continue;
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
                     const int key = kb * 32 + 16 * cc + trow;
@@ -372,9 +385,15 @@ __device__ __forceinline__ int vt_off(int dim, int key) {
            (key & 3);
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ __launch_bounds__(kPPWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(FwdParams p) {
+    // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
+    // time); 2: the window (p.wl, p.wr).
+    constexpr bool CAUSAL = MASK != 0;
+    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
+    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
+    const int wr_ = MASK == 2 ? p.wr : 0;
     constexpr int BN = PPCfg<D>::BN;
     constexpr int NST = kPPStages;
     constexpr int BM = kPPBM;
@@ -405,14 +424,17 @@ void fwd_pp_kernel(FwdParams p) {
     const int wq_last = wq0 + 31;
     const int qrow = wq0 + l32;
 
-    const int kend = CAUSAL ? min(N, q0 + BM) : N;
-    const int T = (kend + BN - 1) / BN;  // tiles of the workgroup
+    // Key tiles of the workgroup: [kt0, kt0 + T).  Masked kernels see keys
+    // q - wl .. q + wr of each query q (causal: wl unbounded, wr = 0).
+    const int kend = CAUSAL ? min(N, q0 + BM + wr_) : N;
+    const int kt0 = WIN ? max(0, q0 - wl_) / BN : 0;
+    const int T = (kend + BN - 1) / BN - kt0;
 
     TileCopy<D, BN, kPPWaves> cp;
     cp.init(w, lane);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
-        if (t < T) cp.issue(Kh, Vh, smem + t * 2 * TILE, smem + t * 2 * TILE + TILE, t * BN, N);
+        if (t < T) cp.issue(Kh, Vh, smem + t * 2 * TILE, smem + t * 2 * TILE + TILE, (kt0 + t) * BN, N);
 
     bf16x8 qreg[D / 16];
 #pragma unroll
@@ -432,17 +454,20 @@ void fwd_pp_kernel(FwdParams p) {
     bf16x8 pb[KB][2];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) pb[kb][0] = pb[kb][1] = bf16x8{};
-    float m = -INFINITY, l = 0.f;
+    // Finite floor for the running max: a row whose first tiles are all
+    // masked (left window edge) keeps exp2(m_old - m_new) defined.
+    float m = -3.0e38f, l = 0.f;
     const int trow = 4 * hi + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+    const int key_lim = CAUSAL ? min(qrow + wr_, N - 1) : N - 1;  // last visible key of this row
+    const int key_lo = WIN ? qrow - wl_ : 0;                     // first visible key
 
     // Number of 32-key blocks of tile j this wave must process (uniform).
     auto active_kb = [&](int j) -> int {
         if (!CAUSAL) return KB;
-        const int kstart = j * BN;
-        if (kstart > wq_last) return 0;
-        return min(KB, (wq_last - kstart) / 32 + 1);
+        const int kstart = (kt0 + j) * BN;
+        if (kstart > wq_last + wr_ || (WIN && kstart + BN - 1 < wq0 - wl_)) return 0;
+        return min(KB, (wq_last + wr_ - kstart) / 32 + 1);
     };
 
     wait_vmem();
@@ -480,7 +505,7 @@ void fwd_pp_kernel(FwdParams p) {
             const int t = step / 2 + 1;
             if (t < T) {
                 bf16* st = smem + (t % NST) * 2 * TILE;
-                cp.issue(Kh, Vh, st, st + TILE, t * BN, N);
+                cp.issue(Kh, Vh, st, st + TILE, (kt0 + t) * BN, N);
             }
         }
     };
@@ -551,15 +576,26 @@ void fwd_pp_kernel(FwdParams p) {
     // ---- V phase j: online softmax of S_j -> P_j (bf16), O rescaled if needed.
     auto phase_v = [&](int j) {
         if (j >= T || active_kb(j) == 0) return;
-        const int kstart = j * BN;
-        const bool need_mask = (CAUSAL && kstart + BN - 1 > wq0) || (kstart + BN > N);
-        if (need_mask) {
+        const int kstart = (kt0 + j) * BN;
+        const bool mask_hi = (CAUSAL && kstart + BN - 1 > wq0 + wr_) || (kstart + BN > N);
+        const bool mask_lo = WIN && kstart < wq_last - wl_;
+        if (mask_hi && !mask_lo) {
             const int lim = key_lim - kstart - 4 * hi;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[kb][r];
+        } else if (mask_lo) {
+            const int lim = key_lim - kstart - 4 * hi;
+            const int lo = key_lo - kstart - 4 * hi;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = kb * 32 + 8 * (r >> 2) + (r & 3);
+                    s[kb][r] = (kk > lim || kk < lo) ? -INFINITY : s[kb][r];
+                }
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -635,9 +671,9 @@ void fwd_pp_kernel(FwdParams p) {
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 hipError_t launch_fwd_pp_t(FwdParams p, hipStream_t stream) {
-    auto kern = fwd_pp_kernel<D, CAUSAL>;
+    auto kern = fwd_pp_kernel<D, MASK>;
     constexpr size_t lds = pp_lds_bytes<D>();
     static bool attr_set = false;
     if (!attr_set) {
@@ -652,9 +688,9 @@ hipError_t launch_fwd_pp_t(FwdParams p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
-    auto kern = fwd_bf16_kernel<D, CAUSAL>;
+    auto kern = fwd_bf16_kernel<D, MASK>;
     constexpr size_t lds = fwd_lds_bytes<D>();
     static bool attr_set = false;  // benign race: setting it twice is harmless
     if (!attr_set) {
@@ -667,291 +703,6 @@ hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
     p.nqb = (p.N + BM - 1) / BM;
     const long long blocks = (long long)p.nqb * p.B * p.Hq;
     hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(FwdCfg<D>::NW * 64), lds, stream, p);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Two-row-block forward (d = 64, 128).  gfx950 LDS delivers about 128 bytes
-// per clock per CU, which is what the matrix cores consume when every
-// 32x32x16 product reads a fresh 1 KB K or V fragment; here each wave owns
-// 64 query rows (two 32-row blocks), so every fragment read from LDS feeds
-// two products and LDS traffic per FLOP halves.  The price is one wave per
-// SIMD, so the softmax has to overlap the matrix products inside the wave:
-// iteration j issues, as one straight-line block,
-//     QK_j (both row blocks)  ->  PV_{j-1} (both row blocks)  ->  softmax_j
-// The softmax of tile j reads S_j and writes P_j while the PV products of
-// tile j-1 are still in flight.  A rescale of O needed by tile j (only when
-// a row max grew) is applied at the top of iteration j+1, before PV_j, so
-// the block stays branch-free.  K/V tiles are 4-buffered in LDS (direct
-// loads, K slabs / V slabs), issued two iterations ahead.
-// ---------------------------------------------------------------------------
-template <int D>
-struct Qr2Cfg;
-template <>
-struct Qr2Cfg<64> {
-    static constexpr int BN = 64;
-};
-template <>
-struct Qr2Cfg<128> {
-    static constexpr int BN = 32;
-};
-constexpr int kQr2Waves = 4;
-constexpr int kQr2Stages = 4;
-constexpr int kQr2BM = 64 * kQr2Waves;
-
-template <int D>
-constexpr size_t qr2_lds_bytes() {
-    return size_t(kQr2Stages) * 2 * Qr2Cfg<D>::BN * D * sizeof(bf16);
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kQr2Waves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_qr2_kernel(FwdParams p) {
-    constexpr int BN = Qr2Cfg<D>::BN;
-    constexpr int NST = kQr2Stages;
-    constexpr int BM = kQr2BM;
-    constexpr int TILE = BN * D;
-    constexpr int KB = BN / 32;
-    extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
-    bf16* smem = reinterpret_cast<bf16*>(smem_raw);
-
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int N = p.N;
-    const float c = p.scale_log2;  // > 0
-
-    int qb, b, h;
-    fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, qb, b, h);
-    const int g = h / (p.Hq / p.Hkv);
-    const size_t qoff = size_t(b * p.Hq + h) * size_t(N) * D;
-    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
-    const bf16* __restrict__ Qh = static_cast<const bf16*>(p.Q) + qoff;
-    const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
-    const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
-    bf16* __restrict__ Oh = static_cast<bf16*>(p.O) + qoff;
-
-    const int q0 = qb * BM;
-    const int wq0 = q0 + 64 * w;  // first query row of this wave (uniform)
-    const int wq_last = wq0 + 63;
-
-    const int kend = CAUSAL ? min(N, q0 + BM) : N;
-    const int T = (kend + BN - 1) / BN;
-
-    TileCopy<D, BN, kQr2Waves> cp;
-    cp.init(w, lane);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-        if (t < T) cp.issue(Kh, Vh, smem + t * 2 * TILE, smem + t * 2 * TILE + TILE, t * BN, N);
-
-    bf16x8 qreg[2][D / 16];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int row = wq0 + 32 * rb + l32;
-#pragma unroll
-        for (int cc = 0; cc < D / 16; ++cc) {
-            u32x4 v = u32x4{0, 0, 0, 0};
-            if (row < N && p.qmode != 2) v = ld16(Qh + size_t(row) * D + 16 * cc + 8 * hi);
-            if (p.qmode == 1) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-            qreg[rb][cc] = as_bf16x8(v);
-        }
-    }
-
-    f32x16 o[2][D / 32];
-    float m[2], l[2], alpha[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[rb][db] = f32x16{};
-        m[rb] = -INFINITY;
-        l[rb] = 0.f;
-        alpha[rb] = 1.f;
-    }
-    bool pending = false;  // O must be rescaled by alpha before the next PV
-    bf16x8 pb[2][KB][2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) pb[rb][kb][0] = pb[rb][kb][1] = bf16x8{};
-
-    const int trow = 4 * hi + ((lane & 15) >> 2);
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int kq_lane = kslab_off<BN>(l32, 8 * hi);      // K A-operand base (elements)
-    const int vt_lane = vslab_off<BN>(trow, tcol);        // V transpose-read base
-    int key_lim[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int row = wq0 + 32 * rb + l32;
-        key_lim[rb] = CAUSAL ? min(row, N - 1) : N - 1;
-    }
-
-    auto active = [&](int j) -> bool { return !CAUSAL || j * BN <= wq_last; };
-
-    // QK of tile j for both row blocks: every K fragment feeds two MFMAs.
-    auto qk = [&](int j, f32x16 (&s)[2][KB]) {
-        const bf16* Ks = smem + (j % NST) * 2 * TILE + kq_lane;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) s[rb][kb] = f32x16{};
-#pragma unroll
-        for (int cc = 0; cc < D / 16; ++cc) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const bf16x8 a = as_bf16x8(ld16(Ks + cc * BN * 16 + kb * 32 * 16));
-                s[0][kb] = mfma_32x32x16(a, qreg[0][cc], s[0][kb]);
-                s[1][kb] = mfma_32x32x16(a, qreg[1][cc], s[1][kb]);
-            }
-        }
-    };
-    // PV of tile j with the P held in pb: every V fragment feeds two MFMAs.
-    auto pv = [&](int j) {
-        const bf16* Vs = smem + (j % NST) * 2 * TILE + TILE + vt_lane;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const bf16x4 v0 = lds_read_tr(Vs + db * BN * 32 + (kb * 32 + 16 * cc) * 32);
-                    const bf16x4 v1 = lds_read_tr(Vs + db * BN * 32 + (kb * 32 + 16 * cc + 8) * 32);
-                    const bf16x8 a = cat(v0, v1);
-                    o[0][db] = mfma_32x32x16(a, pb[0][kb][cc], o[0][db]);
-                    o[1][db] = mfma_32x32x16(a, pb[1][kb][cc], o[1][db]);
-                }
-            }
-        }
-    };
-    // Online softmax of tile j for both row blocks -> pb, alpha, pending.
-    auto softmax = [&](int j, f32x16 (&s)[2][KB], bool need_mask) {
-        const int kstart = j * BN;
-        bool grow = false;
-        float mnew[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            if (need_mask) {
-                const int lim = key_lim[rb] - kstart - 4 * hi;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        s[rb][kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[rb][kb][r];
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
-            mx = half_swap_max(mx) * c;
-            grow = grow || (mx > m[rb] + kTau);
-            mnew[rb] = fmaxf(m[rb], mx);
-        }
-        const bool any_grow = __any(grow);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const float mr = any_grow ? mnew[rb] : m[rb];
-            alpha[rb] = fast_exp2(m[rb] - mr);
-            m[rb] = mr;
-            float rs = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                float e[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    e[r] = fast_exp2(fmaf(s[rb][kb][r], c, -mr));
-                    rs += e[r];
-                }
-                pb[rb][kb][0] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-                pb[rb][kb][1] = to_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
-            }
-            l[rb] = l[rb] * alpha[rb] + rs;
-        }
-        pending = any_grow;
-    };
-
-    wait_vmem();
-    __syncthreads();
-
-    // Iteration j: [rescale O if tile j-1 raised a max] QK_j, PV_{j-1}, softmax_j.
-    // Tile t is copied at iteration t-2 into the buffer of tile t-4 (last read
-    // by PV_{t-4} in iteration t-3) and waited for at the end of iteration t-1.
-    for (int j = 0; j <= T; ++j) {
-        if (j + 2 < T) {
-            const int t = j + 2;
-            bf16* st = smem + (t % NST) * 2 * TILE;
-            cp.issue(Kh, Vh, st, st + TILE, t * BN, N);
-        }
-        if (pending) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) o[rb][db] *= alpha[rb];
-            pending = false;
-        }
-        const bool do_qk = j < T && active(j);
-        const bool do_pv = j >= 1 && active(j - 1);
-        const bool need_mask = do_qk && ((CAUSAL && j * BN + BN - 1 > wq0) || (j * BN + BN > N));
-        f32x16 s[2][KB];
-        if (do_qk && do_pv && !need_mask) {
-            // steady state: one straight-line block
-            qk(j, s);
-            pv(j - 1);
-            softmax(j, s, false);
-        } else {
-            if (do_qk) qk(j, s);
-            if (do_pv) pv(j - 1);
-            if (do_qk) softmax(j, s, need_mask);
-        }
-        // tile j+1 (copied in iteration j-1) must be visible to every wave.
-        // vmcnt counts per wave in issue order: leaving the 2*PER_WAVE copies of
-        // tile j+2 outstanding would need a partial wait; waiting for all keeps
-        // it simple (tile j+2 has had the whole iteration to land).
-        wait_vmem();
-        __syncthreads();
-    }
-    if (pending) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) o[rb][db] *= alpha[rb];
-    }
-
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int qrow = wq0 + 32 * rb + l32;
-        const float lt = half_swap_sum(l[rb]);
-        const float inv = 1.f / lt;
-        if (qrow < N) {
-            bf16* orow = Oh + size_t(qrow) * D;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const bf16x4 v = bf16x4{(bf16)(o[rb][db][4 * jj + 0] * inv), (bf16)(o[rb][db][4 * jj + 1] * inv),
-                                            (bf16)(o[rb][db][4 * jj + 2] * inv), (bf16)(o[rb][db][4 * jj + 3] * inv)};
-                    *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * jj + 4 * hi) = v;
-                }
-            }
-            if (hi == 0 && p.LSE != nullptr)
-                p.LSE[size_t(b * p.Hq + h) * N + qrow] = (m[rb] + fast_log2(lt)) * kLn2;
-        }
-    }
-}
-
-template <int D, bool CAUSAL>
-hipError_t launch_fwd_qr2_t(FwdParams p, hipStream_t stream) {
-    auto kern = fwd_qr2_kernel<D, CAUSAL>;
-    constexpr size_t lds = qr2_lds_bytes<D>();
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    p.nqb = (p.N + kQr2BM - 1) / kQr2BM;
-    const long long blocks = (long long)p.nqb * p.B * p.Hq;
-    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kQr2Waves * 64), lds, stream, p);
     return hipGetLastError();
 }
 
@@ -968,20 +719,22 @@ hipError_t launch_fwd_bf16(FwdParams p, int d, int causal, hipStream_t stream) {
         p.qmode = 2;
         p.scale_log2 = 1.f;
     }
+    // 0: no mask, 1: causal, 2: a general window
+    const int mk = !causal ? 0 : (p.wl >= kUnbounded && p.wr == 0) ? 1 : 2;
+#define FA_FWD_DISPATCH(L, DD) \
+    (mk == 0 ? L<DD, 0>(p, stream) : mk == 1 ? L<DD, 1>(p, stream) : L<DD, 2>(p, stream))
     switch (d) {
-#if FA_FWD_PP == 2
-        case 64: return causal ? launch_fwd_qr2_t<64, true>(p, stream) : launch_fwd_qr2_t<64, false>(p, stream);
-        case 128: return causal ? launch_fwd_qr2_t<128, true>(p, stream) : launch_fwd_qr2_t<128, false>(p, stream);
-#elif FA_FWD_PP
-        case 64: return causal ? launch_fwd_pp_t<64, true>(p, stream) : launch_fwd_pp_t<64, false>(p, stream);
-        case 128: return causal ? launch_fwd_pp_t<128, true>(p, stream) : launch_fwd_pp_t<128, false>(p, stream);
+#if FA_FWD_PP
+        case 64: return FA_FWD_DISPATCH(launch_fwd_pp_t, 64);
+        case 128: return FA_FWD_DISPATCH(launch_fwd_pp_t, 128);
 #else
-        case 64: return causal ? launch_fwd_bf16_t<64, true>(p, stream) : launch_fwd_bf16_t<64, false>(p, stream);
-        case 128: return causal ? launch_fwd_bf16_t<128, true>(p, stream) : launch_fwd_bf16_t<128, false>(p, stream);
+        case 64: return FA_FWD_DISPATCH(launch_fwd_bf16_t, 64);
+        case 128: return FA_FWD_DISPATCH(launch_fwd_bf16_t, 128);
 #endif
-        case 256: return causal ? launch_fwd_bf16_t<256, true>(p, stream) : launch_fwd_bf16_t<256, false>(p, stream);
+        case 256: return FA_FWD_DISPATCH(launch_fwd_bf16_t, 256);
         default: return hipErrorInvalidValue;
     }
+#undef FA_FWD_DISPATCH
 }
 
 }  // namespace fa

@@ -19,8 +19,14 @@ namespace {
 constexpr int kBM32 = 64;  // query rows per workgroup
 constexpr int kBN32 = 32;  // keys per tile
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
+    // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
+    // time); 2: the window (p.wl, p.wr).
+    constexpr bool CAUSAL = MASK != 0;
+    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
+    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
+    const int wr_ = MASK == 2 ? p.wr : 0;
     constexpr int G4 = D / 16;  // float4 groups per lane
     __shared__ __attribute__((aligned(16))) float Ks[kBN32 * D];
     __shared__ __attribute__((aligned(16))) float Vs[kBN32 * D];
@@ -53,9 +59,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     }
     float m = -INFINITY, l = 0.f;
 
-    const int kend = CAUSAL ? min(N, q0 + kBM32) : N;
+    // masked kernels see keys q - wl .. q + wr of each query q
+    const int kend = CAUSAL ? min(N, q0 + kBM32 + wr_) : N;
+    const int kt0 = WIN ? max(0, q0 - wl_) / kBN32 : 0;
     const int ntiles = (kend + kBN32 - 1) / kBN32;
-    for (int kt = 0; kt < ntiles; ++kt) {
+    for (int kt = kt0; kt < ntiles; ++kt) {
         const int kstart = kt * kBN32;
         __syncthreads();
         for (int idx = tid; idx < kBN32 * D / 4; idx += 256) {
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
             acc += __shfl_xor(acc, 2);
             float t = acc * p.scale_log2;
             const int key = kstart + j;
-            if ((CAUSAL && key > qrow) || key >= N) t = -INFINITY;
+            if ((CAUSAL && (key > qrow + wr_ || (WIN && key < qrow - wl_))) || key >= N) t = -INFINITY;
             s[j] = t;
             mx = fmaxf(mx, t);
         }
@@ -121,23 +129,28 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 hipError_t launch_fwd_f32_t(FwdParams p, hipStream_t stream) {
     p.nqb = (p.N + kBM32 - 1) / kBM32;
     const long long blocks = (long long)p.nqb * p.B * p.Hq;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(FwdParams p, int d, int causal, hipStream_t stream) {
+    const int mk = !causal ? 0 : (p.wl >= kUnbounded && p.wr == 0) ? 1 : 2;
+#define FA_F32_DISPATCH(DD) \
+    (mk == 0 ? launch_fwd_f32_t<DD, 0>(p, stream) : mk == 1 ? launch_fwd_f32_t<DD, 1>(p, stream) \
+                                                            : launch_fwd_f32_t<DD, 2>(p, stream))
     switch (d) {
-        case 64: return causal ? launch_fwd_f32_t<64, true>(p, stream) : launch_fwd_f32_t<64, false>(p, stream);
-        case 128: return causal ? launch_fwd_f32_t<128, true>(p, stream) : launch_fwd_f32_t<128, false>(p, stream);
-        case 256: return causal ? launch_fwd_f32_t<256, true>(p, stream) : launch_fwd_f32_t<256, false>(p, stream);
+        case 64: return FA_F32_DISPATCH(64);
+        case 128: return FA_F32_DISPATCH(128);
+        case 256: return FA_F32_DISPATCH(256);
         default: return hipErrorInvalidValue;
     }
+#undef FA_F32_DISPATCH
 }
 
 }  // namespace fa

@@ -19,7 +19,13 @@ struct FwdParams {
     float scale_log2;
     int nqb;    // number of query blocks (filled by the launcher)
     int qmode;  // bf16 kernel: 0 use Q, 1 negate Q, 2 zero Q (filled by the launcher)
+    // Window of the masked kernels: query i sees key j when
+    // i - wl <= j <= i + wr (kUnbounded on a side without a bound).  The
+    // causal mask is (kUnbounded, 0).  Unused by the unmasked kernels.
+    int wl, wr;
 };
+
+constexpr int kUnbounded = 1 << 30;
 
 // Backward launch parameters.
 struct BwdParams {
@@ -37,6 +43,7 @@ struct BwdParams {
     float scale;       // softmax scale
     float scale_log2;  // scale * log2(e)
     int nqb, nkb;      // query / key blocks (filled by the launchers)
+    int wl, wr;        // window of the masked kernels, as FwdParams
 };
 
 // Split key/value forward parameters.  Q [B, Hq, Nq, d], K/V [B, Hkv, Nk, d]
@@ -59,6 +66,7 @@ struct SplitParams {
 // Each launcher enqueues its kernels on `stream` and returns the first HIP
 // error (hipSuccess when everything was enqueued).  Shapes were validated
 // by the caller; d is one of the supported head dims for that launcher.
+// `causal` selects the masked kernels, which apply the window (wl, wr).
 hipError_t launch_fwd_bf16(FwdParams p, int d, int causal, hipStream_t stream);
 hipError_t launch_fwd_f32(FwdParams p, int d, int causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(BwdParams p, int d, int causal, hipStream_t stream);

@@ -62,9 +62,11 @@ def check_half_ulp(got, want, slack, name=""):
 REL_BF16 = 5e-3
 
 
-def check_close(got, want, base, rel=None, name=""):
+def check_close(got, want, base, rel=None, name="", own_ulp=False):
     """max |got - want| <= base, or <= max(base, rel * max|want|) when
-    ``rel`` is given.  Returns the max-abs error."""
+    ``rel`` is given; with ``own_ulp`` each element may also differ by half a
+    bf16 ulp of its exact value (the rounding of the stored bf16 result, on
+    top of the error of the computation).  Returns the max-abs error."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     if got.size == 0:
@@ -72,9 +74,10 @@ def check_close(got, want, base, rel=None, name=""):
     err = np.abs(got - want)
     top = float(np.max(np.abs(want)))
     bound = base if rel is None else max(base, rel * top)
+    excess = err - bound - (bf16_half_ulp(want) if own_ulp else 0.0)
     worst = float(err.max())
-    if worst > bound:
-        i = np.unravel_index(np.argmax(err), err.shape)
-        raise AssertionError(f"{name}: max-abs {worst} > bound {bound} at {i} (got {got[i]}, want {want[i]}, "
-                             f"max|want| {top})")
+    if float(excess.max()) > 0:
+        i = np.unravel_index(np.argmax(excess), err.shape)
+        raise AssertionError(f"{name}: error {err[i]} exceeds its bound by {excess[i]} at {i} (got {got[i]}, "
+                             f"want {want[i]}, max|want| {top}, max-abs {worst})")
     return worst

@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code, name in _lib.STATUS.items():
         assert lib.fa_status_str(code).decode() == name
     assert lib.fa_status_str(12345).decode() == "FA_ERR_UNKNOWN"
-    assert lib.fa_version() == 110
+    assert lib.fa_version() == 120
     assert lib.fa_last_hip_error() == 0
 
 
@@ -210,3 +210,48 @@ def test_merge_rejects(kw, code):
 
 def test_merge_empty_is_noop():
     assert merge(Op=None, Lp=None, O=None, LSE=None, rows=0) == 0
+
+
+def fwdw(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125, wl=4, wr=0,
+             dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_fwd_window(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                                     a["d"], a["scale"], a["wl"], a["wr"], a["dtype"], None)
+
+
+def bwdw(ws_bytes=1 << 20, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, LSE=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE, ws=0x100000,
+             B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125, wl=4, wr=0, dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_bwd_window(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"], a["dV"],
+                                     a["ws"], ws_bytes, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"],
+                                     a["wl"], a["wr"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(wl=-2), "FA_ERR_ARG"),
+    (dict(wr=-3), "FA_ERR_ARG"),
+    (dict(Q=None), "FA_ERR_NULL"),
+    (dict(d=40), "FA_ERR_HEADDIM"),
+    (dict(Hq=3, Hkv=2), "FA_ERR_SHAPE"),
+    (dict(O=MIS), "FA_ERR_ALIGN"),
+    (dict(scale=float("nan")), "FA_ERR_ARG"),
+])
+def test_fwd_window_rejects(kw, code):
+    assert fwdw(**kw) == E[code]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(wl=-5), "FA_ERR_ARG"),
+    (dict(dV=None), "FA_ERR_NULL"),
+    (dict(d=256), "FA_ERR_UNSUPPORTED"),
+    (dict(ws=None), "FA_ERR_WORKSPACE"),
+])
+def test_bwd_window_rejects(kw, code):
+    assert bwdw(**kw) == E[code]
+
+
+def test_window_empty_is_noop():
+    assert fwdw(Q=None, K=None, V=None, O=None, LSE=None, N=0) == 0
+    assert bwdw(Q=None, K=None, V=None, O=None, dO=None, LSE=None, dQ=None, dK=None, dV=None, ws=None, B=0) == 0
