@@ -257,8 +257,8 @@ void bwd_dkdv2_kernel(BwdParams p) {
             for (int kb = 0; kb < KPW; ++kb) sacc[kb] = dpacc[kb] = f32x16{};
 #pragma unroll
             for (int cc = 0; cc < D / 16; ++cc) {
-                const bf16x8 aq = as_bf16x8(ld16(Qs + QL::off(32 * qs + l32, 16 * cc + 8 * hi)));
-                const bf16x8 ao = as_bf16x8(ld16(dOs + QL::off(32 * qs + l32, 16 * cc + 8 * hi)));
+                const bf16x8 aq = as_bf16x8(lds16(Qs + QL::off(32 * qs + l32, 16 * cc + 8 * hi)));
+                const bf16x8 ao = as_bf16x8(lds16(dOs + QL::off(32 * qs + l32, 16 * cc + 8 * hi)));
 #pragma unroll
                 for (int kb = 0; kb < KPW; ++kb) {
                     sacc[kb] = mfma_32x32x16(aq, kreg[kb][cc], sacc[kb]);
@@ -268,8 +268,8 @@ void bwd_dkdv2_kernel(BwdParams p) {
             float lq[16], dq[16];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const f32x4 lv = *reinterpret_cast<const f32x4*>(ls + 32 * qs + 8 * j + 4 * hi);
-                const f32x4 dv4 = *reinterpret_cast<const f32x4*>(dsr + 32 * qs + 8 * j + 4 * hi);
+                const f32x4 lv = lds_f32x4(ls + 32 * qs + 8 * j + 4 * hi);
+                const f32x4 dv4 = lds_f32x4(dsr + 32 * qs + 8 * j + 4 * hi);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     lq[4 * j + e] = lv[e] * kLog2e;
@@ -326,9 +326,13 @@ void bwd_dkdv2_kernel(BwdParams p) {
                 }
             }
         }
+        // This wave's copies of the next tile are done once only the newest
+        // tile's remain; drain this wave's LDS reads (the stage just read is
+        // refilled next) and meet at a plain barrier: a __syncthreads()
+        // fence would also wait for the copy of the newest tile.
         if (more) wait_older();
         else wait_vmem();
-        __syncthreads();
+        barrier_lds();
     }
 
     // Epilogue: lane holds dim db*32 + l32 of keys kw0 + 32kb + 8(r/4) + 4hi + r%4.
@@ -797,8 +801,8 @@ void bwd_dq2_kernel(BwdParams p) {
             s[0] = s[1] = dpt[0] = dpt[1] = f32x16{};
 #pragma unroll
             for (int cc = 0; cc < D / 16; ++cc) {
-                const bf16x8 ak = as_bf16x8(ld16(Ks + KL::off(32 * kb + l32, 16 * cc + 8 * hi)));
-                const bf16x8 av = as_bf16x8(ld16(Vs + KL::off(32 * kb + l32, 16 * cc + 8 * hi)));
+                const bf16x8 ak = as_bf16x8(lds16(Ks + KL::off(32 * kb + l32, 16 * cc + 8 * hi)));
+                const bf16x8 av = as_bf16x8(lds16(Vs + KL::off(32 * kb + l32, 16 * cc + 8 * hi)));
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     s[rb] = mfma_32x32x16(ak, qreg[rb][cc], s[rb]);
@@ -842,9 +846,11 @@ void bwd_dq2_kernel(BwdParams p) {
                 }
             }
         }
+        // as in the dK/dV kernel: own copies of the next tile, LDS reads
+        // drained, plain barrier (no fence waiting for the newest copy)
         if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW) & 15) | (((2 * PPW) >> 4) << 14));
         else wait_vmem();
-        __syncthreads();
+        barrier_lds();
     }
 
 #pragma unroll
