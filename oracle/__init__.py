@@ -10,10 +10,11 @@ The oracle is the plain definition of attention (materialise the score
 matrix, stable row softmax, multiply by V) and the textbook analytic
 backward, in float64, one (batch, query-head) unit at a time, plus
 attention with queries and keys of different lengths, attention over a key
-range, the merge of partial results over disjoint key ranges, and local
-(sliding-window) attention.  Every
-function cites the passage of the source pages it follows; see
-``oracle/attention.py``, ``oracle/splitkv.py`` and ``oracle/window.py``.
+range, the merge of partial results over disjoint key ranges, local
+(sliding-window) attention and batches of packed sequences of different
+lengths.  Every function cites the passage of the source pages it follows;
+see ``oracle/attention.py``, ``oracle/splitkv.py``, ``oracle/window.py`` and
+``oracle/varlen.py``.
 """
 
 from .attention import (
@@ -25,6 +26,7 @@ from .attention import (
     kv_head_of,
 )
 from .splitkv import cross_forward, merge_partials, partial_forward
+from .varlen import varlen_backward, varlen_forward
 from .window import window_backward, window_forward, window_visible
 
 __all__ = [
@@ -40,4 +42,6 @@ __all__ = [
     "window_forward",
     "window_backward",
     "window_visible",
+    "varlen_forward",
+    "varlen_backward",
 ]

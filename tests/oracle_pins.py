@@ -18,6 +18,7 @@ import numpy as np
 
 import oracle.attention as OA
 import oracle.splitkv as OS
+import oracle.varlen as OV
 import oracle.window as OW
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -494,6 +495,85 @@ def check_window_finite_differences(seed=23):
             assert abs(fd - G[ix]) < 1e-7 * max(1.0, abs(fd)), (ix, fd, G[ix])
 
 
+# ---------------------------------------------------------------- packed variable lengths
+
+
+def _pack(rng, lens, Hq, Hkv, d):
+    total = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    Q = rng.standard_normal((Hq, total, d))
+    K = rng.standard_normal((Hkv, total, d))
+    V = rng.standard_normal((Hkv, total, d))
+    return Q, K, V, cu
+
+
+def check_varlen_equal_lengths(seed=24):
+    """B sequences of one length n, packed [H, B*n, d], give the fixed-length
+    batch [B, H, n, d] result, forward and backward, with grouped heads."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, n, d = 3, 4, 2, 6, 5
+    Q, K, V, cu = _pack(rng, [n] * B, Hq, Hkv, d)
+    dO = rng.standard_normal(Q.shape)
+
+    def unpack(X):  # [H, B*n, d] -> [B, H, n, d]
+        return X.reshape(X.shape[0], B, n, -1).transpose(1, 0, 2, 3)
+
+    for causal in (False, True):
+        O, L = OV.varlen_forward(Q, K, V, cu, 0.45, causal)
+        Or, Lr = OA.attention_forward(unpack(Q), unpack(K), unpack(V), 0.45, causal)
+        assert np.max(np.abs(unpack(O) - Or)) < 1e-14
+        assert np.max(np.abs(L.reshape(Hq, B, n).transpose(1, 0, 2) - Lr)) < 1e-13
+        g = OV.varlen_backward(Q, K, V, dO, cu, 0.45, causal)
+        gr = OA.attention_backward(unpack(Q), unpack(K), unpack(V), unpack(dO), 0.45, causal)
+        for a, b in zip(g, gr):
+            assert np.max(np.abs(unpack(a) - b)) < 1e-12
+
+
+def check_varlen_ragged_slices(seed=25):
+    """Ragged lengths (with empty and one-token sequences): every sequence is
+    the square definition on its own rows, so no query sees a key of another
+    sequence; a one-token sequence has O = its V row and LSE = its own score."""
+    rng = np.random.default_rng(seed)
+    lens = [5, 0, 1, 9, 3, 1]
+    Hq, Hkv, d, sc = 4, 2, 4, 0.7
+    Q, K, V, cu = _pack(rng, lens, Hq, Hkv, d)
+    G = Hq // Hkv
+    for causal in (False, True):
+        O, L = OV.varlen_forward(Q, K, V, cu, sc, causal)
+        for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+            for h in range(Hq):
+                o, l = OA.head_forward(Q[h, a:b], K[h // G, a:b], V[h // G, a:b], sc, causal)
+                assert np.max(np.abs(O[h, a:b] - o), initial=0.0) < 1e-14
+                assert np.max(np.abs(L[h, a:b] - l), initial=0.0) < 1e-13
+                if b - a == 1:
+                    assert np.max(np.abs(O[h, a] - V[h // G, a])) < 1e-15
+                    assert abs(L[h, a] - sc * float(Q[h, a] @ K[h // G, a])) < 1e-13
+
+
+def check_varlen_finite_differences(seed=26):
+    """Central differences of <dO, O> over a ragged, grouped-head pack."""
+    rng = np.random.default_rng(seed)
+    Q, K, V, cu = _pack(rng, [3, 1, 4], 4, 2, 3)
+    dO = rng.standard_normal(Q.shape)
+    sc = 0.9
+    h = 1e-6
+    for causal in (False, True):
+        dQ, dK, dV = OV.varlen_backward(Q, K, V, dO, cu, sc, causal)
+
+        def loss(q, k, v):
+            return float((OV.varlen_forward(q, k, v, cu, sc, causal)[0] * dO).sum())
+
+        for X, Gr in ((Q, dQ), (K, dK), (V, dV)):
+            for _ in range(6):
+                ix = tuple(int(rng.integers(0, s)) for s in X.shape)
+                Xp, Xm = X.copy(), X.copy()
+                Xp[ix] += h
+                Xm[ix] -= h
+                fd = (loss(*[Xp if Y is X else Y for Y in (Q, K, V)]) -
+                      loss(*[Xm if Y is X else Y for Y in (Q, K, V)])) / (2 * h)
+                assert abs(fd - Gr[ix]) < 1e-7 * max(1.0, abs(fd)), (ix, fd, Gr[ix])
+
+
 ALL_CHECKS = [
     check_four_token_tiles_consistent,
     check_four_token_recurrence_values,
@@ -516,4 +596,7 @@ ALL_CHECKS = [
     check_window_special_cases,
     check_window_rows_are_slices,
     check_window_finite_differences,
+    check_varlen_equal_lengths,
+    check_varlen_ragged_slices,
+    check_varlen_finite_differences,
 ]

@@ -9,6 +9,7 @@ import pytest
 
 import oracle.attention as OA
 import oracle.splitkv as OS
+import oracle.varlen as OV
 import oracle.window as OW
 import oracle_pins
 
@@ -187,6 +188,51 @@ def _merge_plain_mean(O_parts, LSE_parts):
     O, L = OS_orig["merge_partials"](O_parts, LSE_parts)
     return np.asarray(O_parts, float).mean(axis=0), L
 
+
+def _varlen_fwd_factory(kind):
+    def fwd(Q, K, V, cu, scale, causal):
+        Q, K, V = (np.asarray(x, float) for x in (Q, K, V))
+        Hq, Hkv = Q.shape[0], K.shape[0]
+        cu = [int(x) for x in cu]
+        O, L = np.zeros((Hq, Q.shape[1], V.shape[2])), np.zeros((Hq, Q.shape[1]))
+        for a, b in zip(cu[:-1], cu[1:]):
+            if b == a:
+                continue
+            ka = max(0, a - 1) if kind == "leak_previous" else a
+            for h in range(Hq):
+                g = OA.kv_head_of(h, Hq, Hkv)
+                if kind == "leak_previous":
+                    # keys of the previous sequence's last token visible too
+                    q, k, v = Q[h, a:b], K[g, ka:b], V[g, ka:b]
+                    s = scale * (q @ k.T)
+                    if causal:
+                        i = np.arange(b - a)[:, None] + (a - ka)
+                        j = np.arange(b - ka)[None, :]
+                        s = np.where(j > i, -np.inf, s)
+                    p, m, l = OA._row_softmax(s)
+                    O[h, a:b], L[h, a:b] = p @ v, m + np.log(l)
+                else:  # "kv_head_by_query": the query head indexes K/V directly (mod H_kv)
+                    O[h, a:b], L[h, a:b] = OA.head_forward(Q[h, a:b], K[h % Hkv, a:b], V[h % Hkv, a:b], scale, causal)
+        return O, L
+
+    return fwd
+
+
+def _varlen_bwd_overwrite(Q, K, V, dO, cu, scale, causal):
+    Q, K, V, dO = (np.asarray(x, float) for x in (Q, K, V, dO))
+    Hq, Hkv = Q.shape[0], K.shape[0]
+    cu = [int(x) for x in cu]
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    for a, b in zip(cu[:-1], cu[1:]):
+        if b == a:
+            continue
+        for h in range(Hq):
+            g = OA.kv_head_of(h, Hq, Hkv)
+            dq, dk, dv = OA.head_backward(Q[h, a:b], K[g, a:b], V[g, a:b], dO[h, a:b], scale, causal)
+            dQ[h, a:b], dK[g, a:b], dV[g, a:b] = dq, dk, dv
+    return dQ, dK, dV
+
+
 MUTANTS = {
     "scale_dropped": ("_scores", _scores_no_scale),
     "scale_twice": ("_scores", _scores_scale_twice),
@@ -213,6 +259,9 @@ MUTANTS = {
     "window_left_off_by_one": (OW, "window_visible", _window_off_by_one),
     "window_sides_swapped": (OW, "window_visible", _window_swapped),
     "window_bwd_missing_row_term": (OW, "window_backward", _window_bwd_no_rowterm),
+    "varlen_leaks_previous_sequence": (OV, "varlen_forward", _varlen_fwd_factory("leak_previous")),
+    "varlen_kv_head_by_query_index": (OV, "varlen_forward", _varlen_fwd_factory("kv_head_by_query")),
+    "varlen_group_grads_overwritten": (OV, "varlen_backward", _varlen_bwd_overwrite),
 }
 
 
