@@ -161,6 +161,43 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O,
                   int window_left, int window_right, int dtype, void* stream);
 
 /*
+ * Packed variable-length batches.  The interview Q&A page (app.wittybyte.ai,
+ * "FlashAttention1", scaling-challenges answer) names uneven work across the
+ * GPU's cores for variable sequence lengths and gives no layout.  Reading:
+ * the batch's sequences are packed back to back, per head, with no padding:
+ *   Q, O      [H_q, total, d]     K, V   [H_kv, total, d]
+ *   LSE       float32 [H_q, total]   (fa_fwd_varlen: may be NULL)
+ *   cu_seqlens  int32 [batch + 1], DEVICE memory: cu[0] = 0, non-decreasing,
+ *               cu[batch] = total; sequence b is rows cu[b] .. cu[b+1]-1 of
+ *               every head
+ *   max_seqlen  >= every cu[b+1] - cu[b], <= FA_MAX_N (sizes the grid)
+ * Each sequence is attended to on its own, exactly as one batch entry of
+ * fa_fwd / fa_bwd (causal: within the sequence); no query sees a key of
+ * another sequence.  An empty sequence is allowed.  dQ is shaped as Q, dK and
+ * dV as K; the backward workspace holds H_q * total floats
+ * (fa_bwd_varlen_workspace_size).
+ * The host cannot read cu_seqlens, so it is not checked: the kernels clamp
+ * each offset into [0, total] and each length to max_seqlen, which keeps
+ * every access inside the buffers above, but offsets that break the rules
+ * give unspecified values (rows past max_seqlen of a longer sequence, and
+ * rows outside every sequence, are not written).
+ * batch == 0, total == 0 or max_seqlen == 0: nothing to do (FA_OK).  Other
+ * constraints (heads, d, dtype, alignment, d = 256 backward) as fa_fwd /
+ * fa_bwd; cu_seqlens must be 4-byte aligned; total < 0 is FA_ERR_SHAPE.
+ */
+int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                  const int* cu_seqlens, int batch, int total, int max_seqlen,
+                  int H_q, int H_kv, int d, float scale, int causal, int dtype, void* stream);
+/* Bytes of device workspace fa_bwd_varlen needs; 0 when total <= 0 or the
+ * arguments are invalid. */
+size_t fa_bwd_varlen_workspace_size(int total, int H_q, int H_kv, int d, int dtype);
+int fa_bwd_varlen(const void* Q, const void* K, const void* V, const void* O,
+                  const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                  void* workspace, size_t workspace_bytes, const int* cu_seqlens,
+                  int batch, int total, int max_seqlen, int H_q, int H_kv, int d,
+                  float scale, int causal, int dtype, void* stream);
+
+/*
  * Split key/value forward: N_q queries against N_k keys, the keys cut into
  * ranges whose partial results are merged -- for decoding steps and other
  * inputs with few queries per head (N_q much smaller than N_k) or few

@@ -42,6 +42,9 @@ EXPORTS = (
     "fa_lse_merge",
     "fa_fwd_window",
     "fa_bwd_window",
+    "fa_fwd_varlen",
+    "fa_bwd_varlen_workspace_size",
+    "fa_bwd_varlen",
 )
 
 
@@ -99,6 +102,14 @@ def load():
     lib.fa_fwd_window.restype = _i
     lib.fa_bwd_window.argtypes = [_vp] * 10 + [ctypes.c_size_t, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp]
     lib.fa_bwd_window.restype = _i
+    # Q K V O LSE cu | batch total max_seqlen H_q H_kv d | scale | causal dtype | stream
+    lib.fa_fwd_varlen.argtypes = [_vp] * 6 + [_i] * 6 + [_f, _i, _i, _vp]
+    lib.fa_fwd_varlen.restype = _i
+    lib.fa_bwd_varlen_workspace_size.argtypes = [_i] * 5
+    lib.fa_bwd_varlen_workspace_size.restype = ctypes.c_size_t
+    # Q K V O dO LSE dQ dK dV workspace | bytes | cu | batch total max_seqlen H_q H_kv d | scale | causal dtype | stream
+    lib.fa_bwd_varlen.argtypes = [_vp] * 10 + [ctypes.c_size_t, _vp] + [_i] * 6 + [_f, _i, _i, _vp]
+    lib.fa_bwd_varlen.restype = _i
     _lib = lib
     return lib
 

@@ -199,3 +199,77 @@ def bwd_window(q, k, v, o, lse, do, window, scale=None, workspace=None):
     )
     _lib.check(st, "fa_bwd_window")
     return dq, dk, dv
+
+
+def _check_varlen(q, k, v, cu_seqlens, *extra):
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be packed [H, total, d]")
+    if not q.is_cuda:
+        raise ValueError("tensors must be on a HIP device")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t in (k, v, *extra):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on the same device")
+        if t.dtype != q.dtype:
+            raise TypeError("all tensors must share one dtype")
+    for t in (q, k, v, *extra):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [H, total, d]")
+    Hq, total, d = q.shape
+    if k.shape[1] != total or k.shape[2] != d or v.shape != k.shape:
+        raise ValueError("k, v must be [H_kv, total, d] matching q")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of batch + 1 offsets")
+    if cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous tensor on the tensors' device")
+    return cu_seqlens.numel() - 1, total, Hq, k.shape[0], d
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=True, out=None, lse=None):
+    """Forward over packed sequences of different lengths.
+
+    q [H_q, total, d], k, v [H_kv, total, d]; sequence b is rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 (int32, on the device) of every head;
+    max_seqlen bounds every length.  Returns (o like q, lse float32
+    [H_q, total]).
+    """
+    batch, total, Hq, Hkv, d = _check_varlen(q, k, v, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((Hq, total), device=q.device, dtype=torch.float32)
+    st = _lib.load().fa_fwd_varlen(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        lse.data_ptr() or None, cu_seqlens.data_ptr() or None, batch, total, int(max_seqlen), Hq, Hkv, d,
+        float(scale), int(bool(causal)), _DTYPES[q.dtype], _stream(q.device),
+    )
+    _lib.check(st, "fa_fwd_varlen")
+    return o, lse
+
+
+def bwd_varlen_workspace_size(total, Hq, Hkv, d, dtype=torch.bfloat16):
+    return int(_lib.load().fa_bwd_varlen_workspace_size(total, Hq, Hkv, d, _DTYPES[dtype]))
+
+
+def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, scale=None, causal=True, workspace=None):
+    """Backward of ``fwd_varlen``: returns (dq, dk, dv) shaped like q, k, v."""
+    batch, total, Hq, Hkv, d = _check_varlen(q, k, v, cu_seqlens, o, do)
+    if lse.dtype != torch.float32 or lse.shape != (Hq, total) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [H_q, total]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bwd_varlen_workspace_size(total, Hq, Hkv, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    st = _lib.load().fa_bwd_varlen(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        do.data_ptr() or None, lse.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,
+        dv.data_ptr() or None, workspace.data_ptr() or None, workspace.numel(), cu_seqlens.data_ptr() or None,
+        batch, total, int(max_seqlen), Hq, Hkv, d, float(scale), int(bool(causal)), _DTYPES[q.dtype],
+        _stream(q.device),
+    )
+    _lib.check(st, "fa_bwd_varlen")
+    return dq, dk, dv

@@ -67,8 +67,10 @@ bool window_bounds(int left, int right, int& wl, int& wr) {
     return !(left < 0 && right < 0);  // (-1, -1) is no mask
 }
 
+// Fixed-length batches pass cu == nullptr; packed sequences pass the device
+// offsets, the packed row count `total` and the longest length as N.
 int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N, int d,
-             float scale, int left, int right, int dtype, void* stream) {
+             float scale, int left, int right, int dtype, void* stream, const int* cu = nullptr, int total = 0) {
     if (B == 0 || N == 0) return FA_OK;
     if (!Q || !K || !V || !O) return FA_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 16))
@@ -83,6 +85,8 @@ int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, i
     p.Hq = H_q;
     p.Hkv = H_kv;
     p.N = N;
+    p.cu = cu;
+    p.total = total;
     p.scale_log2 = scale * kLog2e;
     const bool masked = window_bounds(left, right, p.wl, p.wr);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -93,14 +97,15 @@ int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, i
 
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
              void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d,
-             float scale, int left, int right, int dtype, void* stream) {
+             float scale, int left, int right, int dtype, void* stream, const int* cu = nullptr, int total = 0) {
     if (dtype == FA_BF16 && d == 256) return FA_ERR_UNSUPPORTED;
     if (B == 0 || N == 0) return FA_OK;
     if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
         !aligned(LSE, 16) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16))
         return FA_ERR_ALIGN;
-    if (!workspace || workspace_bytes < fa::bwd_workspace_bytes(B, H_q, N)) return FA_ERR_WORKSPACE;
+    const long long rows = cu != nullptr ? (long long)total : (long long)B * N;
+    if (!workspace || workspace_bytes < fa::bwd_workspace_bytes(H_q, rows)) return FA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
     fa::BwdParams p{};
     p.Q = Q;
@@ -117,6 +122,8 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
     p.Hq = H_q;
     p.Hkv = H_kv;
     p.N = N;
+    p.cu = cu;
+    p.total = total;
     p.scale = scale;
     p.scale_log2 = scale * kLog2e;
     const bool masked = window_bounds(left, right, p.wl, p.wr);
@@ -124,6 +131,18 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
     hipError_t e = (dtype == FA_BF16) ? fa::launch_bwd_bf16(p, d, masked, s) : fa::launch_bwd_f32(p, d, masked, s);
     if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
     if (e != hipSuccess) return hip_failure(e);
+    return FA_OK;
+}
+
+// Checks of the packed (variable-length) entry points beyond validate():
+// the packed row count and the offsets array.  Returns FA_OK or an error;
+// `work` tells whether there is anything to compute.
+int validate_varlen(const int* cu, int batch, int total, int max_seqlen, bool& work) {
+    if (total < 0) return FA_ERR_SHAPE;
+    work = batch > 0 && total > 0 && max_seqlen > 0;
+    if (!work) return FA_OK;
+    if (!cu) return FA_ERR_NULL;
+    if (!aligned(cu, 4)) return FA_ERR_ALIGN;
     return FA_OK;
 }
 
@@ -138,7 +157,7 @@ bool split_grid_ok(int B, int Hq, int Hkv, int Nq, int parts) {
 
 extern "C" {
 
-int fa_version(void) { return 120; }
+int fa_version(void) { return 130; }
 
 const char* fa_status_str(int status) {
     switch (status) {
@@ -176,7 +195,7 @@ int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L
 size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, int dtype) {
     if (validate(B, H_q, H_kv, N, d, 1.0f, 0, dtype) != FA_OK) return 0;
     if (B == 0 || N == 0) return 0;
-    return fa::bwd_workspace_bytes(B, H_q, N);
+    return fa::bwd_workspace_bytes(H_q, (long long)B * N);
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
@@ -196,6 +215,35 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
     if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
     return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H_q, H_kv, N, d, scale,
                     window_left, window_right, dtype, stream);
+}
+
+int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE, const int* cu_seqlens, int batch,
+                  int total, int max_seqlen, int H_q, int H_kv, int d, float scale, int causal, int dtype,
+                  void* stream) {
+    int st = validate(batch, H_q, H_kv, max_seqlen, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    bool work = false;
+    if ((st = validate_varlen(cu_seqlens, batch, total, max_seqlen, work)) != FA_OK || !work) return st;
+    return fwd_impl(Q, K, V, O, LSE, batch, H_q, H_kv, max_seqlen, d, scale, causal ? -1 : -2, causal ? 0 : -2, dtype,
+                    stream, cu_seqlens, total);
+}
+
+size_t fa_bwd_varlen_workspace_size(int total, int H_q, int H_kv, int d, int dtype) {
+    if (validate(1, H_q, H_kv, 0, d, 1.0f, 0, dtype) != FA_OK || total <= 0) return 0;
+    return fa::bwd_workspace_bytes(H_q, total);
+}
+
+int fa_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                  void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, const int* cu_seqlens,
+                  int batch, int total, int max_seqlen, int H_q, int H_kv, int d, float scale, int causal, int dtype,
+                  void* stream) {
+    int st = validate(batch, H_q, H_kv, max_seqlen, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    if (dtype == FA_BF16 && d == 256) return FA_ERR_UNSUPPORTED;
+    bool work = false;
+    if ((st = validate_varlen(cu_seqlens, batch, total, max_seqlen, work)) != FA_OK || !work) return st;
+    return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, batch, H_q, H_kv, max_seqlen, d,
+                    scale, causal ? -1 : -2, causal ? 0 : -2, dtype, stream, cu_seqlens, total);
 }
 
 size_t fa_fwd_split_workspace_size(int B, int H_q, int H_kv, int N_q, int N_k, int d, int num_splits, int dtype) {

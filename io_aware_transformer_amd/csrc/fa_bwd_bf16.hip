@@ -44,8 +44,8 @@
 
 namespace fa {
 
-size_t bwd_workspace_bytes(int B, int Hq, int N) {
-    const size_t d_bytes = size_t(B) * size_t(Hq) * size_t(N) * sizeof(float);
+size_t bwd_workspace_bytes(int Hq, long long rows) {
+    const size_t d_bytes = size_t(Hq) * size_t(rows) * sizeof(float);
     return (d_bytes + 255) / 256 * 256;
 }
 
@@ -137,17 +137,19 @@ void bwd_dkdv2_kernel(BwdParams p) {
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int N = p.N;
     const float c = p.scale_log2;
     const int units = p.B * p.Hkv;
     const int slot = blockIdx.x / units;
     const int unit = remap_unit(blockIdx.x - slot * units, units);
     const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
     const int G = p.Hq / p.Hkv;
+    const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
+    const int N = sq.n;
     const int kstart = slot * dk_keys_per_wg<D>();
+    if (kstart >= N) return;  // past the end of a shorter packed sequence (whole workgroup)
     const int kw0 = kstart + 32 * KPW * w;  // first key of this wave (uniform)
 
-    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const size_t kvoff = sq.kvrow(g) * D;
     const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
     const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
 
@@ -192,7 +194,7 @@ void bwd_dkdv2_kernel(BwdParams p) {
     auto issue = [&](int t) {
         const int hq = g * G + t / per_head;
         const int q0 = (qt_first + t % per_head) * BQ;
-        const size_t row0 = size_t(b * p.Hq + hq) * size_t(N) + q0;
+        const size_t row0 = sq.qrow(hq) + q0;
         unsigned char* st = smem_raw + (t % NST) * SB;
         const uint32_t bytes = uint32_t(N - q0) * uint32_t(D * 2);
         const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const bf16*>(p.Q) + row0 * D, bytes);
@@ -403,17 +405,19 @@ void bwd_dkdv3_kernel(BwdParams p) {
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int N = p.N;
     const float c = p.scale_log2;
     const int units = p.B * p.Hkv;
     const int slot = blockIdx.x / units;
     const int unit = remap_unit(blockIdx.x - slot * units, units);
     const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
     const int G = p.Hq / p.Hkv;
+    const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
+    const int N = sq.n;
     const int kstart = slot * kDk3KeysPerWg;
+    if (kstart >= N) return;  // past the end of a shorter packed sequence (whole workgroup)
     const int kw0 = kstart + 32 * w;  // first key of this wave (uniform)
 
-    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const size_t kvoff = sq.kvrow(g) * D;
     const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
     const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
 
@@ -462,7 +466,7 @@ void bwd_dkdv3_kernel(BwdParams p) {
     auto tile_copy = [&](int t) {
         const int hq = g * G + t / per_head;
         const int q0 = tile_q0(t);
-        const size_t row0 = size_t(b * p.Hq + hq) * size_t(N) + q0;
+        const size_t row0 = sq.qrow(hq) + q0;
         const uint32_t bytes = uint32_t(N - q0) * uint32_t(D * 2);
         TileCopy tc;
         tc.q = make_rsrc(static_cast<const bf16*>(p.Q) + row0 * D, bytes);
@@ -703,7 +707,6 @@ void bwd_dq2_kernel(BwdParams p) {
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int N = p.N;
     const float c = p.scale_log2;
     const int units = p.B * p.Hq;
     const int slot = blockIdx.x / units;
@@ -711,8 +714,11 @@ void bwd_dq2_kernel(BwdParams p) {
     const int qb = CAUSAL ? p.nqb - 1 - slot : slot;
     const int b = unit / p.Hq, h = unit - (unit / p.Hq) * p.Hq;
     const int g = h / (p.Hq / p.Hkv);
-    const size_t qrows = size_t(b * p.Hq + h) * size_t(N);
-    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
+    const int N = sq.n;
+    if (qb * kDqBM >= N) return;  // past the end of a shorter packed sequence (whole workgroup)
+    const size_t qrows = sq.qrow(h);
+    const size_t kvoff = sq.kvrow(g) * D;
     const bf16* __restrict__ Qh = static_cast<const bf16*>(p.Q) + qrows * D;
     const bf16* __restrict__ dOh = static_cast<const bf16*>(p.dO) + qrows * D;
     const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
@@ -884,7 +890,8 @@ hipError_t set_lds(K kern, size_t bytes, bool& done) {
 template <int D, int MASK>
 hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     // 1. D_i = dO_i . O_i
-    const long long rows = (long long)p.B * p.Hq * p.N;
+    // Every query row of every head: [B, Hq, N] rows, or [Hq, total] packed.
+    const long long rows = p.cu != nullptr ? (long long)p.Hq * p.total : (long long)p.B * p.Hq * p.N;
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(unsigned((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
                        static_cast<const bf16*>(p.O), static_cast<const bf16*>(p.dO), p.Drow, rows);

@@ -29,6 +29,37 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Rows of one attention unit (batch entry or packed sequence b) in the
+// query-side and key-side buffers.  Fixed-length batch ([B, H, N, d]): head h
+// of entry b starts at row (b*H + h)*N and has N rows.  Packed sequences
+// ([H, total, d] with offsets cu[0..B]): sequence b of head h starts at row
+// h*total + cu[b] and has cu[b+1] - cu[b] rows.  The offsets are clamped
+// into [0, total] and the length to at most N (the bound the grid was sized
+// for), so every access stays inside the buffers whatever the offsets hold.
+struct SeqSpan {
+    size_t qbase, kvbase, hstride;
+    int n;  // rows of this unit
+    __device__ __forceinline__ size_t qrow(int h) const { return qbase + size_t(h) * hstride; }
+    __device__ __forceinline__ size_t kvrow(int g) const { return kvbase + size_t(g) * hstride; }
+};
+
+__device__ __forceinline__ SeqSpan seq_span(const int* cu, int total, int Hq, int Hkv, int N, int b) {
+    SeqSpan s;
+    if (cu != nullptr) {
+        const int a = min(max(cu[b], 0), total);
+        const int e = min(max(cu[b + 1], a), total);
+        s.qbase = s.kvbase = size_t(a);
+        s.hstride = size_t(total);
+        s.n = min(e - a, N);
+    } else {
+        s.qbase = size_t(b) * size_t(Hq) * size_t(N);
+        s.kvbase = size_t(b) * size_t(Hkv) * size_t(N);
+        s.hstride = size_t(N);
+        s.n = N;
+    }
+    return s;
+}
+
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

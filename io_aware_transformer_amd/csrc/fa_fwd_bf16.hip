@@ -173,14 +173,16 @@ void fwd_bf16_kernel(FwdParams p) {
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int N = p.N;
     const float c = p.scale_log2;  // > 0
 
     int qb, b, h;
     fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, qb, b, h);
     const int g = h / (p.Hq / p.Hkv);
-    const size_t qoff = size_t(b * p.Hq + h) * size_t(N) * D;
-    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
+    const int N = sq.n;
+    if (qb * BM >= N) return;  // past the end of a shorter packed sequence (whole workgroup)
+    const size_t qoff = sq.qrow(h) * D;
+    const size_t kvoff = sq.kvrow(g) * D;
     const bf16* __restrict__ Qh = static_cast<const bf16*>(p.Q) + qoff;
     const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
     const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
@@ -335,7 +337,7 @@ void fwd_bf16_kernel(FwdParams p) {
                 *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * j + 4 * hi) = v;
             }
         }
-        if (hi == 0 && p.LSE != nullptr) p.LSE[size_t(b * p.Hq + h) * N + qrow] = (m + fast_log2(lt)) * kLn2;
+        if (hi == 0 && p.LSE != nullptr) p.LSE[sq.qrow(h) + qrow] = (m + fast_log2(lt)) * kLn2;
     }
 }
 
@@ -406,14 +408,16 @@ void fwd_pp_kernel(FwdParams p) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int grp = w >> 2;                                  // 0: group A, 1: group B
     const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int N = p.N;
     const float c = p.scale_log2;  // > 0
 
     int qb, b, h;
     fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, qb, b, h);
     const int g = h / (p.Hq / p.Hkv);
-    const size_t qoff = size_t(b * p.Hq + h) * size_t(N) * D;
-    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
+    const int N = sq.n;
+    if (qb * BM >= N) return;  // past the end of a shorter packed sequence (whole workgroup)
+    const size_t qoff = sq.qrow(h) * D;
+    const size_t kvoff = sq.kvrow(g) * D;
     const bf16* __restrict__ Qh = static_cast<const bf16*>(p.Q) + qoff;
     const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
     const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
@@ -667,7 +671,7 @@ void fwd_pp_kernel(FwdParams p) {
                 *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * jj + 4 * hi) = v;
             }
         }
-        if (hi == 0 && p.LSE != nullptr) p.LSE[size_t(b * p.Hq + h) * N + qrow] = (m + fast_log2(lt)) * kLn2;
+        if (hi == 0 && p.LSE != nullptr) p.LSE[sq.qrow(h) + qrow] = (m + fast_log2(lt)) * kLn2;
     }
 }
 

@@ -34,15 +34,17 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63;
     const int row = lane >> 2, part = lane & 3;
-    const int N = p.N;
     const int units = p.B * p.Hq;
     const int slot = blockIdx.x / units;
     const int unit = blockIdx.x - slot * units;
     const int qb = CAUSAL ? p.nqb - 1 - slot : slot;
     const int b = unit / p.Hq, h = unit - (unit / p.Hq) * p.Hq;
     const int g = h / (p.Hq / p.Hkv);
-    const size_t qoff = size_t(b * p.Hq + h) * size_t(N) * D;
-    const size_t kvoff = size_t(b * p.Hkv + g) * size_t(N) * D;
+    const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
+    const int N = sq.n;
+    if (qb * kBM32 >= N) return;  // past the end of a shorter packed sequence (whole workgroup)
+    const size_t qoff = sq.qrow(h) * D;
+    const size_t kvoff = sq.kvrow(g) * D;
     const float* __restrict__ Qh = static_cast<const float*>(p.Q) + qoff;
     const float* __restrict__ Kh = static_cast<const float*>(p.K) + kvoff;
     const float* __restrict__ Vh = static_cast<const float*>(p.V) + kvoff;
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < G4; ++i)
             *reinterpret_cast<f32x4*>(Oh + size_t(qrow) * D + 16 * i + 4 * part) = o[i] * inv;
-        if (part == 0 && p.LSE != nullptr) p.LSE[size_t(b * p.Hq + h) * N + qrow] = (m + log2f(l)) * kLn2;
+        if (part == 0 && p.LSE != nullptr) p.LSE[sq.qrow(h) + qrow] = (m + log2f(l)) * kLn2;
     }
 }
 

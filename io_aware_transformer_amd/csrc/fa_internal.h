@@ -23,6 +23,12 @@ struct FwdParams {
     // i - wl <= j <= i + wr (kUnbounded on a side without a bound).  The
     // causal mask is (kUnbounded, 0).  Unused by the unmasked kernels.
     int wl, wr;
+    // Packed sequences: when cu is non-null, Q/O are [Hq, total, d], K/V
+    // [Hkv, total, d], LSE [Hq, total], and sequence b is rows cu[b] ..
+    // cu[b+1]-1 of every head (cu is a device array of B + 1 ints); N is then
+    // the longest sequence (the grid's row bound).
+    const int* cu;
+    int total;
 };
 
 constexpr int kUnbounded = 1 << 30;
@@ -44,6 +50,8 @@ struct BwdParams {
     float scale_log2;  // scale * log2(e)
     int nqb, nkb;      // query / key blocks (filled by the launchers)
     int wl, wr;        // window of the masked kernels, as FwdParams
+    const int* cu;     // packed sequences, as FwdParams (Drow is then [Hq, total])
+    int total;
 };
 
 // Split key/value forward parameters.  Q [B, Hq, Nq, d], K/V [B, Hkv, Nk, d]
@@ -72,8 +80,10 @@ hipError_t launch_fwd_f32(FwdParams p, int d, int causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(BwdParams p, int d, int causal, hipStream_t stream);
 hipError_t launch_bwd_f32(BwdParams p, int d, int causal, hipStream_t stream);
 
-// Workspace bytes of the backward for these sizes (D term only).
-size_t bwd_workspace_bytes(int B, int Hq, int N);
+// Workspace bytes of the backward for `rows` query rows per head, summed
+// over the batch (B * N for a fixed-length batch, total for packed
+// sequences): the D term only.
+size_t bwd_workspace_bytes(int Hq, long long rows);
 
 // Split forward: partial kernel (launch_fwd_split_bf16, d in {64, 128}) and
 // the merge of partials (launch_lse_merge, d in {64, 128, 256}, output bf16

@@ -5,10 +5,11 @@ imports this module, and this module imports nothing from the HIP library.
 
 Sources (cited by page title and section):
 
-* FlashAttention interview Q&A (app.wittybyte.ai, "FlashAttention1"): its
-  list of extensions includes variable-length sequences within a batch, and
-  its implementation answer mentions handling them.  The pages give no
-  layout.
+* FlashAttention interview Q&A (app.wittybyte.ai, "FlashAttention1"): the
+  answer on scaling challenges names uneven work across the GPU's cores for
+  variable sequence lengths, to be met by dynamic load balancing or sequence
+  bucketing; the integration answer asks for inputs formatted for block-wise
+  processing.  The pages give no layout.
 * Each sequence is attended to on its own with the definition of
   ``oracle.attention`` (deep-dive page, standard attention Steps 1-3):
   no query sees a key of another sequence.

@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code, name in _lib.STATUS.items():
         assert lib.fa_status_str(code).decode() == name
     assert lib.fa_status_str(12345).decode() == "FA_ERR_UNKNOWN"
-    assert lib.fa_version() == 120
+    assert lib.fa_version() == 130
     assert lib.fa_last_hip_error() == 0
 
 
@@ -255,3 +255,76 @@ def test_bwd_window_rejects(kw, code):
 def test_window_empty_is_noop():
     assert fwdw(Q=None, K=None, V=None, O=None, LSE=None, N=0) == 0
     assert bwdw(Q=None, K=None, V=None, O=None, dO=None, LSE=None, dQ=None, dK=None, dV=None, ws=None, B=0) == 0
+
+
+def fwdv(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, cu=FAKE, batch=2, total=40, mx=30, Hq=2, Hkv=1, d=64,
+             scale=0.125, causal=1, dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_fwd_varlen(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["cu"], a["batch"], a["total"],
+                                     a["mx"], a["Hq"], a["Hkv"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+def bwdv(ws_bytes=1 << 20, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, LSE=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE, ws=0x100000, cu=FAKE,
+             batch=2, total=40, mx=30, Hq=2, Hkv=1, d=64, scale=0.125, causal=1, dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_bwd_varlen(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"], a["dV"],
+                                     a["ws"], ws_bytes, a["cu"], a["batch"], a["total"], a["mx"], a["Hq"], a["Hkv"],
+                                     a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), "FA_ERR_NULL"),
+    (dict(Q=None), "FA_ERR_NULL"),
+    (dict(cu=FAKE + 2), "FA_ERR_ALIGN"),
+    (dict(O=MIS), "FA_ERR_ALIGN"),
+    (dict(total=-1), "FA_ERR_SHAPE"),
+    (dict(batch=-1), "FA_ERR_SHAPE"),
+    (dict(mx=-1), "FA_ERR_SHAPE"),
+    (dict(mx=(1 << 22) + 1), "FA_ERR_SHAPE"),
+    (dict(Hq=3, Hkv=2), "FA_ERR_SHAPE"),
+    (dict(d=96), "FA_ERR_HEADDIM"),
+    (dict(dtype=5), "FA_ERR_DTYPE"),
+    (dict(causal=2), "FA_ERR_ARG"),
+    (dict(scale=float("inf")), "FA_ERR_ARG"),
+])
+def test_fwd_varlen_rejects(kw, code):
+    assert fwdv(**kw) == E[code]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), "FA_ERR_NULL"),
+    (dict(dK=None), "FA_ERR_NULL"),
+    (dict(d=256), "FA_ERR_UNSUPPORTED"),
+    (dict(ws=None), "FA_ERR_WORKSPACE"),
+    (dict(total=-3), "FA_ERR_SHAPE"),
+    (dict(dtype=_lib.FA_FP32), "FA_ERR_UNSUPPORTED"),
+])
+def test_bwd_varlen_rejects(kw, code):
+    assert bwdv(**kw) == E[code]
+
+
+def test_bwd_varlen_workspace_too_small():
+    need = _lib.load().fa_bwd_varlen_workspace_size(40, 2, 1, 64, _lib.FA_BF16)
+    assert need == (2 * 40 * 4 + 255) // 256 * 256
+    assert bwdv(ws_bytes=need - 1) == E["FA_ERR_WORKSPACE"]
+    assert bwdv(ws=0x100010) == E["FA_ERR_ALIGN"]
+
+
+def test_varlen_workspace_size():
+    f = _lib.load().fa_bwd_varlen_workspace_size
+    assert f(16384, 16, 16, 128, _lib.FA_BF16) == 16 * 16384 * 4
+    assert f(0, 16, 16, 128, _lib.FA_BF16) == 0
+    assert f(100, 16, 3, 128, _lib.FA_BF16) == 0  # invalid heads
+    assert f(100, 16, 16, 48, _lib.FA_BF16) == 0  # invalid d
+
+
+def test_varlen_empty_is_noop():
+    none = dict(Q=None, K=None, V=None, O=None, LSE=None, cu=None)
+    assert fwdv(batch=0, **none) == 0
+    assert fwdv(total=0, **none) == 0
+    assert fwdv(mx=0, **none) == 0
+    gnone = dict(none, dO=None, dQ=None, dK=None, dV=None, ws=None)
+    assert bwdv(batch=0, **gnone) == 0
+    assert bwdv(total=0, **gnone) == 0

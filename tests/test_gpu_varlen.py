@@ -1,0 +1,193 @@
+"""Packed variable-length batches, forward and backward, against the fp64
+oracle, through the C ABI (fa_fwd_varlen / fa_bwd_varlen)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import REL_BF16, TOL, check_close, f64, maxabs, require_gpu
+from io_aware_transformer_amd import bwd, bwd_varlen, fwd, fwd_varlen, inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+BF = torch.bfloat16
+
+# Ragged mixes: empty and one-token sequences, tails of every tile size, one
+# sequence longer than a query block of every kernel, equal lengths.
+LENGTHS = {
+    "one": [1],
+    "empties": [0, 5, 0],
+    "mix": [77, 1, 300, 64, 129],
+    "equal": [256, 256, 256],
+    "long_tail": [513, 2, 1000, 31],
+}
+HEADS = [(2, 1), (4, 4), (8, 2)]
+
+
+def _run_fwd(q, k, v, cu, scale, causal):
+    n = cu[1:] - cu[:-1]
+    mx = int(n.max()) if n.numel() else 0
+    o, lse = fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), mx, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("heads", HEADS, ids=lambda h: f"Hq{h[0]}Hkv{h[1]}")
+@pytest.mark.parametrize("mix", sorted(LENGTHS))
+def test_varlen_fwd(mix, heads, causal, d):
+    require_gpu()
+    lens = LENGTHS[mix]
+    q, k, v, cu = inputs.make_varlen(lens, *heads, d, BF, 4000 + d + sum(lens))
+    sc = d ** -0.5
+    o, lse = _run_fwd(q, k, v, cu, sc, causal)
+    want_o, want_l = oracle.varlen_forward(f64(q), f64(k), f64(v), cu.numpy(), sc, causal)
+    assert maxabs(f64(o), want_o) <= TOL[BF]["out"]
+    assert maxabs(lse.numpy(), want_l) <= TOL[BF]["lse"]
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_fwd_fp32(causal, d):
+    require_gpu()
+    lens = LENGTHS["mix"]
+    q, k, v, cu = inputs.make_varlen(lens, 4, 2, d, torch.float32, 4100 + d)
+    o, lse = _run_fwd(q, k, v, cu, d ** -0.5, causal)
+    want_o, want_l = oracle.varlen_forward(f64(q), f64(k), f64(v), cu.numpy(), d ** -0.5, causal)
+    assert maxabs(f64(o), want_o) <= TOL[torch.float32]["out"]
+    assert maxabs(lse.numpy(), want_l) <= TOL[torch.float32]["lse"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("heads", HEADS, ids=lambda h: f"Hq{h[0]}Hkv{h[1]}")
+@pytest.mark.parametrize("mix", sorted(LENGTHS))
+def test_varlen_bwd(mix, heads, causal, d):
+    require_gpu()
+    lens = LENGTHS[mix]
+    q, k, v, do, cu = inputs.make_varlen(lens, *heads, d, BF, 5000 + d + sum(lens), with_grad=True)
+    sc = d ** -0.5
+    mx = max(lens)
+    qd, kd, vd, dod, cud = (t.to(DEV) for t in (q, k, v, do, cu))
+    o, lse = fwd_varlen(qd, kd, vd, cud, mx, scale=sc, causal=causal)
+    dq, dk, dv = bwd_varlen(qd, kd, vd, o, lse, dod, cud, mx, scale=sc, causal=causal)
+    torch.cuda.synchronize()
+    gq, gk, gv = oracle.varlen_backward(f64(q), f64(k), f64(v), f64(do), cu.numpy(), sc, causal)
+    base = TOL[BF]["out"]
+    check_close(f64(dq), gq, base, REL_BF16, "dQ")
+    check_close(f64(dk), gk, base, REL_BF16, "dK")
+    check_close(f64(dv), gv, base, REL_BF16, "dV")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equal_lengths_match_fixed_entry(causal, d):
+    """B sequences of one length run the same kernels as fa_fwd / fa_bwd on
+    the [B, H, N, d] batch: results are bit-identical after the layout
+    change."""
+    require_gpu()
+    B, Hq, Hkv, N = 3, 4, 2, 333
+    q, k, v, do = inputs.make(B, Hq, Hkv, N, d, BF, 17, with_grad=True)
+
+    def pack(x):  # [B, H, N, d] -> [H, B*N, d]
+        return x.permute(1, 0, 2, 3).reshape(x.shape[1], B * N, d).contiguous()
+
+    def unpack(x):  # [H, B*N, d] -> [B, H, N, d]
+        return x.reshape(x.shape[0], B, N, d).permute(1, 0, 2, 3).contiguous()
+
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device=DEV)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = fwd(qd, kd, vd, causal=causal)
+    g = bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    po, plse = fwd_varlen(pack(qd), pack(kd), pack(vd), cu, N, causal=causal)
+    pg = bwd_varlen(pack(qd), pack(kd), pack(vd), po, plse, pack(dod), cu, N, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(unpack(po), o)
+    assert torch.equal(plse.reshape(Hq, B, N).permute(1, 0, 2), lse)
+    for x, y in zip(pg, g):
+        assert torch.equal(unpack(x), y)
+
+
+def test_varlen_max_seqlen_above_longest():
+    """A max_seqlen larger than every length only adds workgroups that exit
+    at once: results are bit-identical."""
+    require_gpu()
+    lens = LENGTHS["mix"]
+    q, k, v, do, cu = (t.to(DEV) for t in inputs.make_varlen(lens, 4, 2, 128, BF, 23, with_grad=True))
+    a = fwd_varlen(q, k, v, cu, max(lens), causal=True)
+    b = fwd_varlen(q, k, v, cu, 4 * max(lens) + 1, causal=True)
+    ga = bwd_varlen(q, k, v, a[0], a[1], do, cu, max(lens), causal=True)
+    gb = bwd_varlen(q, k, v, b[0], b[1], do, cu, 4 * max(lens) + 1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for x, y in zip(ga, gb):
+        assert torch.equal(x, y)
+
+
+def test_varlen_other_sequences_do_not_leak():
+    """Changing every other sequence's Q, K, V leaves one sequence's outputs
+    and gradients bit-identical."""
+    require_gpu()
+    lens = [200, 333, 150]
+    q, k, v, do, cu = inputs.make_varlen(lens, 4, 2, 64, BF, 29, with_grad=True)
+    q2, k2, v2, do2, _ = inputs.make_varlen(lens, 4, 2, 64, BF, 30, with_grad=True)
+    a, b = int(cu[1]), int(cu[2])  # the middle sequence
+    for x, y in ((q2, q), (k2, k), (v2, v), (do2, do)):
+        x[:, a:b] = y[:, a:b]
+    res = []
+    for t in ((q, k, v, do), (q2, k2, v2, do2)):
+        qd, kd, vd, dod = (x.to(DEV) for x in t)
+        o, lse = fwd_varlen(qd, kd, vd, cu.to(DEV), 333, causal=True)
+        g = bwd_varlen(qd, kd, vd, o, lse, dod, cu.to(DEV), 333, causal=True)
+        torch.cuda.synchronize()
+        res.append([x[:, a:b].cpu() for x in (o, lse, *g)])
+    for x, y in zip(*res):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", sorted(inputs.VARLEN_PRESETS))
+def test_varlen_full_size_sampled(name):
+    """The benchmark packs: complete outputs and gradients of sampled
+    sequences and heads against the oracle on those sequences."""
+    require_gpu()
+    p = inputs.VARLEN_PRESETS[name]
+    lens = p.lengths
+    q, k, v, do, cu = inputs.make_varlen_preset(p)
+    qd, kd, vd, dod, cud = (t.to(DEV) for t in (q, k, v, do, cu))
+    o, lse = fwd_varlen(qd, kd, vd, cud, max(lens), scale=p.scale, causal=p.causal)
+    dq, dk, dv = bwd_varlen(qd, kd, vd, o, lse, dod, cud, max(lens), scale=p.scale, causal=p.causal)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (t.cpu() for t in (o, lse, dq, dk, dv))
+    tol = TOL[BF]["out"]
+    longest = int(np.argmax(lens))
+    for s, h in ((longest, 0), (len(lens) - 1, p.Hq - 1), (1, 5)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        g = h // (p.Hq // p.Hkv)
+        qq, kk, vv, dd = f64(q[h, a:b]), f64(k[g, a:b]), f64(v[g, a:b]), f64(do[h, a:b])
+        want_o, want_l = oracle.head_forward(qq, kk, vv, p.scale, p.causal)
+        assert maxabs(f64(o[h, a:b]), want_o) <= tol, (s, h)
+        assert maxabs(lse[h, a:b].numpy(), want_l) <= TOL[BF]["lse"], (s, h)
+        gq, gk, gv = oracle.head_backward(qq, kk, vv, dd, p.scale, p.causal)
+        assert maxabs(f64(dq[h, a:b]), gq) <= tol, ("dQ", s, h)
+        if p.Hq == p.Hkv:
+            assert maxabs(f64(dk[g, a:b]), gk) <= tol, ("dK", s, h)
+            assert maxabs(f64(dv[g, a:b]), gv) <= tol, ("dV", s, h)
+
+
+@pytest.mark.parametrize("case", ["batch0", "total0", "all_empty", "max0"])
+def test_varlen_nothing_to_do(case):
+    require_gpu()
+    d, Hq, Hkv = 64, 2, 1
+    total = 0 if case in ("total0", "all_empty") else 16
+    q = torch.zeros((Hq, total, d), device=DEV, dtype=BF)
+    k = torch.zeros((Hkv, total, d), device=DEV, dtype=BF)
+    cu = {"batch0": [0], "total0": [0, 0], "all_empty": [0, 0, 0], "max0": [0, 16]}[case]
+    cu = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    mx = 0 if case == "max0" else 16
+    o = torch.full_like(q, 3.0)
+    fwd_varlen(q, k, k.clone(), cu, mx, out=o)
+    torch.cuda.synchronize()
+    assert torch.all(o == 3.0)  # untouched: nothing was computed
