@@ -236,13 +236,147 @@ def bench_split(args, p):
     print(json.dumps(line), flush=True)
 
 
+def varlen_flops(p):
+    """Forward FLOP of a packed batch: 4*H*n^2*d per sequence of n tokens
+    (halved for causal, the convention of ``flops``)."""
+    f = sum(4.0 * p.Hq * n * n * p.d for n in p.lengths)
+    return f / 2 if p.causal else f
+
+
+def cpu_baseline_varlen(p, budget_s):
+    """The fp64 oracle on (sequence, head) units of the pack, sequences taken
+    in order, forward and backward, until ``budget_s`` of CPU work is done."""
+    import numpy as np
+
+    import oracle
+    from io_aware_transformer_amd import inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, k, v, do, cu = inputs.make_varlen_preset(p)
+    done_flops, units = 0.0, 0
+    t0 = time.perf_counter()
+    for s in range(len(p.lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        x = [t[0, a:b].float().numpy().astype(np.float64) for t in (q, k, v, do)]
+        oracle.head_forward(x[0], x[1], x[2], p.scale, p.causal)
+        oracle.head_backward(*x, p.scale, p.causal)
+        n = b - a
+        done_flops += 3.5 * 4.0 * n * n * p.d / (2 if p.causal else 1)
+        units += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{units} (sequence, head) units of the pack (fwd+bwd) in {dt:.1f} s, same FLOP "
+                      f"convention as the GPU line"}
+
+
+def bench_varlen(args, p):
+    """Packed variable-length batch: one step is fa_fwd_varlen then
+    fa_bwd_varlen over the whole pack.  The same sequences padded to the
+    longest one and run through fa_fwd / fa_bwd are timed beside it."""
+    import torch
+
+    from io_aware_transformer_amd import bwd, bwd_varlen, bwd_varlen_workspace_size, fwd, fwd_varlen, inputs
+
+    dev = torch.device("cuda:0")
+    lens = p.lengths
+    mx = max(lens)
+    q, k, v, do, cu = (t.to(dev) for t in inputs.make_varlen_preset(p))
+    o = torch.empty_like(q)
+    lse = torch.empty((p.Hq, p.total), device=dev, dtype=torch.float32)
+    ws = torch.empty(max(1, bwd_varlen_workspace_size(p.total, p.Hq, p.Hkv, p.d)), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(f, b, steps, warmup):
+        for _ in range(warmup):
+            f()
+            b()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in evs:
+            e[0].record(stream)
+            f()
+            e[1].record(stream)
+            b()
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        return [e[0].elapsed_time(e[1]) for e in evs], [e[1].elapsed_time(e[2]) for e in evs]
+
+    fwd_ms, bwd_ms = run(lambda: fwd_varlen(q, k, v, cu, mx, scale=p.scale, causal=p.causal, out=o, lse=lse),
+                         lambda: bwd_varlen(q, k, v, o, lse, do, cu, mx, scale=p.scale, causal=p.causal,
+                                            workspace=ws),
+                         args.steps, args.warmup)
+    ff = varlen_flops(p)
+    fa, ba = sum(fwd_ms) / len(fwd_ms), sum(bwd_ms) / len(bwd_ms)
+    ms = fa + ba
+    value = 3.5 * ff / (ms * 1e-3) / 1e12
+
+    # Padded comparison: B = number of sequences, N = the longest length.
+    B = len(lens)
+    pq = torch.zeros((B, p.Hq, mx, p.d), device=dev, dtype=q.dtype)
+    pk = torch.zeros((B, p.Hkv, mx, p.d), device=dev, dtype=q.dtype)
+    pv, pdo = torch.zeros_like(pk), torch.zeros_like(pq)
+    c = cu.cpu()
+    for s in range(B):
+        a, b = int(c[s]), int(c[s + 1])
+        pq[s, :, : b - a] = q[:, a:b]
+        pk[s, :, : b - a] = k[:, a:b]
+        pv[s, :, : b - a] = v[:, a:b]
+        pdo[s, :, : b - a] = do[:, a:b]
+    po, plse = fwd(pq, pk, pv, scale=p.scale, causal=p.causal)
+    pf, pb = run(lambda: fwd(pq, pk, pv, scale=p.scale, causal=p.causal, out=po, lse=plse),
+                 lambda: bwd(pq, pk, pv, po, plse, pdo, scale=p.scale, causal=p.causal),
+                 max(5, args.steps // 4), 2)
+    pms = sum(pf) / len(pf) + sum(pb) / len(pb)
+    line = {
+        "metric": "attention fwd/bwd TFLOP/s (bf16, causal, d=128, N=2K-8K) + % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic: seeded N(0,1) Q, K, V, dO rounded to bf16, seeded log-uniform lengths, resident in HBM",
+        "config": {"workload": f"{p.name}: fwd+bwd packed variable-length {p.dtype} "
+                               f"{'causal' if p.causal else 'non-causal'} {len(lens)} sequences, total={p.total} "
+                               f"(lengths {min(lens)}..{mx}) H_q={p.Hq} H_kv={p.Hkv} d={p.d}",
+                   "lengths": lens},
+        "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(ff / (fa * 1e-3) / 1e12, 2),
+        "fwd_ms_p10_p90": [round(pct(fwd_ms, 10), 5), round(pct(fwd_ms, 90), 5)],
+        "bwd_tflops": round(2.5 * ff / (ba * 1e-3) / 1e12, 2),
+        "bwd_ms_p10_p90": [round(pct(bwd_ms, 10), 5), round(pct(bwd_ms, 90), 5)],
+        "roofline": {"bound": "mfma", "kernel": "fwd_pp_kernel (fa_fwd_varlen)",
+                     "achieved": round(ff / (fa * 1e-3) / 1e12, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(ff / (fa * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(fa, 5)},
+        "padded": {"B": B, "N": mx, "ms_per_step": round(pms, 5),
+                   "useful_tflops": round(3.5 * ff / (pms * 1e-3) / 1e12, 2),
+                   "speedup_of_packed": round(pms / ms, 3)},
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline_varlen(p, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--preset", default="c2", help="input preset (default c2: B8 H16 N2048 d128 bf16 causal; "
-                                                    "s1..s3: split key/value forward on decoding shapes)")
+                                                    "s1..s3: split key/value forward on decoding shapes; "
+                                                    "v1, v2: packed variable-length batches)")
     ap.add_argument("--passes", default="fwd,bwd", help="comma list of fwd,bwd")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline budget (0 disables)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -288,6 +422,9 @@ def main():
         return
     if args.preset in inputs.SPLIT_PRESETS:
         bench_split(args, inputs.SPLIT_PRESETS[args.preset])
+        return
+    if args.preset in inputs.VARLEN_PRESETS:
+        bench_varlen(args, inputs.VARLEN_PRESETS[args.preset])
         return
     p = inputs.PRESETS[args.preset]
     passes = [x for x in args.passes.split(",") if x]

@@ -71,10 +71,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O
     if (row < rows && part == 0) Drow[row] = acc;
 }
 
-// XCD-aware unit remap shared by the two main kernels (see the forward).
-__device__ __forceinline__ int remap_unit(int u, int units) {
-    return (units % 8 == 0) ? (u & 7) * (units >> 3) + (u >> 3) : u;
-}
 
 // ---------------------------------------------------------------- bwd_dkdv v2
 // One workgroup of 4 waves per (batch, kv head, block of 32*KPW*4 keys); each
@@ -140,7 +136,7 @@ void bwd_dkdv2_kernel(BwdParams p) {
     const float c = p.scale_log2;
     const int units = p.B * p.Hkv;
     const int slot = blockIdx.x / units;
-    const int unit = remap_unit(blockIdx.x - slot * units, units);
+    const int unit = order_unit(blockIdx.x - slot * units, units, p.Hkv, p.cu != nullptr);
     const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
     const int G = p.Hq / p.Hkv;
     const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
@@ -408,7 +404,7 @@ void bwd_dkdv3_kernel(BwdParams p) {
     const float c = p.scale_log2;
     const int units = p.B * p.Hkv;
     const int slot = blockIdx.x / units;
-    const int unit = remap_unit(blockIdx.x - slot * units, units);
+    const int unit = order_unit(blockIdx.x - slot * units, units, p.Hkv, p.cu != nullptr);
     const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
     const int G = p.Hq / p.Hkv;
     const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
@@ -710,7 +706,7 @@ void bwd_dq2_kernel(BwdParams p) {
     const float c = p.scale_log2;
     const int units = p.B * p.Hq;
     const int slot = blockIdx.x / units;
-    const int unit = remap_unit(blockIdx.x - slot * units, units);
+    const int unit = order_unit(blockIdx.x - slot * units, units, p.Hq, p.cu != nullptr);
     const int qb = CAUSAL ? p.nqb - 1 - slot : slot;
     const int b = unit / p.Hq, h = unit - (unit / p.Hq) * p.Hq;
     const int g = h / (p.Hq / p.Hkv);

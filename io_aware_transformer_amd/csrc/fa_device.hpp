@@ -60,6 +60,24 @@ __device__ __forceinline__ SeqSpan seq_span(const int* cu, int total, int Hq, in
     return s;
 }
 
+// Workgroup unit slot u (0 <= u < units = B*H; workgroups are dealt to the
+// 8 XCDs round-robin, so u % 8 picks the XCD) -> unit b*H + h.
+// Fixed-length batch (every unit costs the same): when units % 8 == 0,
+// consecutive units go to one XCD so heads sharing K/V share its L2.
+// Packed sequences (units of very different cost): every XCD takes the same
+// slice of heads of every sequence -- heads [x*H/8, (x+1)*H/8) on XCD x when
+// H % 8 == 0 (grouped query heads stay together when their group divides
+// H/8), round-robin otherwise -- so no XCD gets a long sequence's heads alone.
+__device__ __forceinline__ int order_unit(int u, int units, int H, bool packed) {
+    if (packed) {
+        if (H % 8 != 0) return u;
+        const int hp = H >> 3, x = u & 7, j = u >> 3;
+        const int b = j / hp;
+        return b * H + x * hp + (j - b * hp);
+    }
+    return (units % 8 == 0) ? (u & 7) * (units >> 3) + (u >> 3) : u;
+}
+
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -87,15 +87,13 @@ constexpr size_t fwd_lds_bytes() {
 }
 
 // Workgroup id -> (query block, batch, head).  Heaviest causal query blocks
-// are issued first.  Workgroups are dealt round-robin to the 8 XCDs; when
-// the number of (batch, head) units is a multiple of 8, consecutive units
-// are remapped onto one XCD so heads sharing K/V share that XCD's L2.
-__device__ __forceinline__ void fwd_decompose(int id, int units, int nqb, int Hq, bool causal, int& qb, int& b,
-                                              int& h) {
+// are issued first; units are ordered over the XCDs by order_unit.
+__device__ __forceinline__ void fwd_decompose(int id, int units, int nqb, int Hq, bool causal, bool packed, int& qb,
+                                              int& b, int& h) {
     const int slot = id / units;
     const int u = id - slot * units;
     qb = causal ? nqb - 1 - slot : slot;
-    const int unit = (units % 8 == 0) ? (u & 7) * (units >> 3) + (u >> 3) : u;
+    const int unit = order_unit(u, units, Hq, packed);
     b = unit / Hq;
     h = unit - b * Hq;
 }
@@ -176,7 +174,7 @@ void fwd_bf16_kernel(FwdParams p) {
     const float c = p.scale_log2;  // > 0
 
     int qb, b, h;
-    fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, qb, b, h);
+    fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, p.cu != nullptr, qb, b, h);
     const int g = h / (p.Hq / p.Hkv);
     const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
     const int N = sq.n;
@@ -411,7 +409,7 @@ void fwd_pp_kernel(FwdParams p) {
     const float c = p.scale_log2;  // > 0
 
     int qb, b, h;
-    fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, qb, b, h);
+    fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, p.cu != nullptr, qb, b, h);
     const int g = h / (p.Hq / p.Hkv);
     const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
     const int N = sq.n;
