@@ -177,6 +177,30 @@ def test_varlen_full_size_sampled(name):
             assert maxabs(f64(dv[g, a:b]), gv) <= tol, ("dV", s, h)
 
 
+@pytest.mark.parametrize("heads", [(16, 8), (24, 8), (12, 4), (32, 16)], ids=lambda h: f"Hq{h[0]}Hkv{h[1]}")
+def test_varlen_head_orders(heads):
+    """Head counts that take each branch of the unit order over the XCDs
+    (head slices when H is a multiple of 8, round-robin otherwise, for the
+    query-head and the kv-head grids): every unit is computed exactly once."""
+    require_gpu()
+    lens = [150, 3, 290, 64]
+    d = 64
+    q, k, v, do, cu = inputs.make_varlen(lens, *heads, d, BF, 6000 + heads[0], with_grad=True)
+    sc = d ** -0.5
+    qd, kd, vd, dod, cud = (t.to(DEV) for t in (q, k, v, do, cu))
+    o, lse = fwd_varlen(qd, kd, vd, cud, max(lens), scale=sc, causal=True)
+    dq, dk, dv = bwd_varlen(qd, kd, vd, o, lse, dod, cud, max(lens), scale=sc, causal=True)
+    torch.cuda.synchronize()
+    want_o, want_l = oracle.varlen_forward(f64(q), f64(k), f64(v), cu.numpy(), sc, True)
+    assert maxabs(f64(o), want_o) <= TOL[BF]["out"]
+    assert maxabs(lse.cpu().numpy(), want_l) <= TOL[BF]["lse"]
+    gq, gk, gv = oracle.varlen_backward(f64(q), f64(k), f64(v), f64(do), cu.numpy(), sc, True)
+    base = TOL[BF]["out"]
+    check_close(f64(dq), gq, base, REL_BF16, "dQ")
+    check_close(f64(dk), gk, base, REL_BF16, "dK")
+    check_close(f64(dv), gv, base, REL_BF16, "dV")
+
+
 @pytest.mark.parametrize("case", ["batch0", "total0", "all_empty", "max0"])
 def test_varlen_nothing_to_do(case):
     require_gpu()
