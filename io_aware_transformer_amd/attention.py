@@ -19,11 +19,29 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _on_device(t):
+    """Checked last, after every shape / dtype / buffer check, so that all
+    argument validation can be exercised without a GPU."""
+    if not t.is_cuda:
+        raise ValueError("tensors must be on a HIP device")
+
+
+def _buffer(t, shape, dtype, device, name):
+    """A caller-supplied output buffer (``out=``, ``lse=``) must be exactly
+    what the kernels write: contiguous, of this shape, dtype and device;
+    None allocates one."""
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, device=device, dtype=dtype)
+    if tuple(t.shape) != shape or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {device} "
+                         f"(got {t.dtype} {tuple(t.shape)} on {t.device}, contiguous={t.is_contiguous()})")
+    return t
+
+
 def _check(q, k, v, *extra):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
-    if not q.is_cuda:
-        raise ValueError("tensors must be on a HIP device")
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for t in (k, v, *extra):
@@ -45,9 +63,9 @@ def fwd(q, k, v, scale=None, causal=True, out=None, lse=None):
     B, Hq, Hkv, N, d = _check(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    o = _buffer(out, q.shape, q.dtype, q.device, "out")
+    lse = _buffer(lse, (B, Hq, N), torch.float32, q.device, "lse")
+    _on_device(q)
     lib = _lib.load()
     st = lib.fa_fwd(
         q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
@@ -73,6 +91,7 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=True, workspace=None):
     ws_bytes = bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    _on_device(q)
     lib = _lib.load()
     st = lib.fa_bwd(
         q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
@@ -87,8 +106,6 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=True, workspace=None):
 def _check_split(q, k, v):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
-    if not q.is_cuda:
-        raise ValueError("tensors must be on a HIP device")
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for t in (k, v):
@@ -123,12 +140,12 @@ def fwd_split(q, k, v, scale=None, causal=True, num_splits=0, out=None, lse=None
     B, Hq, Hkv, Nq, Nk, d = _check_split(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
+    o = _buffer(out, q.shape, q.dtype, q.device, "out")
+    lse = _buffer(lse, (B, Hq, Nq), torch.float32, q.device, "lse")
     ws_bytes = fwd_split_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    _on_device(q)
     lib = _lib.load()
     st = lib.fa_fwd_split(
         q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
@@ -144,15 +161,17 @@ def lse_merge(o_parts, lse_parts, dtype=torch.bfloat16, out=None, lse=None):
     [P, ...] -> (o [..., d] of ``dtype``, lse float32 [...])."""
     if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
         raise TypeError("partials must be float32")
-    if not (o_parts.is_cuda and lse_parts.is_cuda and o_parts.is_contiguous() and lse_parts.is_contiguous()):
-        raise ValueError("partials must be contiguous device tensors")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()) or lse_parts.device != o_parts.device:
+        raise ValueError("partials must be contiguous tensors on one device")
     if o_parts.shape[:-1] != lse_parts.shape or o_parts.dim() < 2:
         raise ValueError("o_parts must be [P, ..., d] and lse_parts [P, ...]")
     P, d = o_parts.shape[0], o_parts.shape[-1]
     rows = lse_parts[0].numel()
-    o = torch.empty(o_parts.shape[1:], device=o_parts.device, dtype=dtype) if out is None else out
-    if lse is None:
-        lse = torch.empty(lse_parts.shape[1:], device=o_parts.device, dtype=torch.float32)
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    o = _buffer(out, o_parts.shape[1:], dtype, o_parts.device, "out")
+    lse = _buffer(lse, lse_parts.shape[1:], torch.float32, o_parts.device, "lse")
+    _on_device(o_parts)
     st = _lib.load().fa_lse_merge(
         o_parts.data_ptr() or None, lse_parts.data_ptr() or None, P, rows, d, o.data_ptr() or None,
         lse.data_ptr() or None, _DTYPES[dtype], _stream(o_parts.device),
@@ -168,9 +187,9 @@ def fwd_window(q, k, v, window, scale=None, out=None, lse=None):
     left, right = (int(x) for x in window)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    o = _buffer(out, q.shape, q.dtype, q.device, "out")
+    lse = _buffer(lse, (B, Hq, N), torch.float32, q.device, "lse")
+    _on_device(q)
     st = _lib.load().fa_fwd_window(
         q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
         lse.data_ptr() or None, B, Hq, Hkv, N, d, float(scale), left, right, _DTYPES[q.dtype], _stream(q.device),
@@ -191,6 +210,7 @@ def bwd_window(q, k, v, o, lse, do, window, scale=None, workspace=None):
     ws_bytes = bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    _on_device(q)
     st = _lib.load().fa_bwd_window(
         q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
         do.data_ptr() or None, lse.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,
@@ -204,8 +224,6 @@ def bwd_window(q, k, v, o, lse, do, window, scale=None, workspace=None):
 def _check_varlen(q, k, v, cu_seqlens, *extra):
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be packed [H, total, d]")
-    if not q.is_cuda:
-        raise ValueError("tensors must be on a HIP device")
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for t in (k, v, *extra):
@@ -237,9 +255,9 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=True, out=Non
     batch, total, Hq, Hkv, d = _check_varlen(q, k, v, cu_seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((Hq, total), device=q.device, dtype=torch.float32)
+    o = _buffer(out, q.shape, q.dtype, q.device, "out")
+    lse = _buffer(lse, (Hq, total), torch.float32, q.device, "lse")
+    _on_device(q)
     st = _lib.load().fa_fwd_varlen(
         q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
         lse.data_ptr() or None, cu_seqlens.data_ptr() or None, batch, total, int(max_seqlen), Hq, Hkv, d,
@@ -264,6 +282,7 @@ def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, scale=None, causal=T
     ws_bytes = bwd_varlen_workspace_size(total, Hq, Hkv, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    _on_device(q)
     st = _lib.load().fa_bwd_varlen(
         q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
         do.data_ptr() or None, lse.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,

@@ -56,15 +56,19 @@ int split_parts(int B, int Hq, int Hkv, int Nq, int Nk, int d, int splits) {
 }
 
 // Window bounds -> kernel form.  -1: unbounded; -2: no mask at all (the
-// unmasked kernels).  Returns whether the masked kernels are needed.
-bool window_bounds(int left, int right, int& wl, int& wr) {
+// unmasked kernels).  A bound of N - 1 or more hides nothing on its side
+// (|i - j| <= N - 1 for rows of one sequence), so it is the unbounded case:
+// this keeps the kernels' index arithmetic (row +- bound) far from int
+// overflow for any int bound.  Returns whether the masked kernels are needed.
+bool window_bounds(int left, int right, int N, int& wl, int& wr) {
     if (left == -2 && right == -2) {
         wl = wr = fa::kUnbounded;
         return false;
     }
-    wl = left < 0 ? fa::kUnbounded : left;
-    wr = right < 0 ? fa::kUnbounded : right;
-    return !(left < 0 && right < 0);  // (-1, -1) is no mask
+    const bool lu = left < 0 || left >= N - 1, ru = right < 0 || right >= N - 1;
+    wl = lu ? fa::kUnbounded : left;
+    wr = ru ? fa::kUnbounded : right;
+    return !(lu && ru);  // unbounded on both sides is no mask
 }
 
 // Fixed-length batches pass cu == nullptr; packed sequences pass the device
@@ -88,7 +92,7 @@ int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, i
     p.cu = cu;
     p.total = total;
     p.scale_log2 = scale * kLog2e;
-    const bool masked = window_bounds(left, right, p.wl, p.wr);
+    const bool masked = window_bounds(left, right, N, p.wl, p.wr);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = (dtype == FA_BF16) ? fa::launch_fwd_bf16(p, d, masked, s) : fa::launch_fwd_f32(p, d, masked, s);
     if (e != hipSuccess) return hip_failure(e);
@@ -126,7 +130,7 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
     p.total = total;
     p.scale = scale;
     p.scale_log2 = scale * kLog2e;
-    const bool masked = window_bounds(left, right, p.wl, p.wr);
+    const bool masked = window_bounds(left, right, N, p.wl, p.wr);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = (dtype == FA_BF16) ? fa::launch_bwd_bf16(p, d, masked, s) : fa::launch_bwd_f32(p, d, masked, s);
     if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
@@ -154,6 +158,42 @@ bool split_grid_ok(int B, int Hq, int Hkv, int Nq, int parts) {
 }
 
 }  // namespace
+
+namespace fa {
+
+hipError_t set_max_dynamic_lds(const void* kern, size_t bytes, DeviceOnce& once) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+    if (bit != 0 && (once.done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+    if (e == hipSuccess && bit != 0) once.done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
+int device_cu_count() {
+    constexpr int kDefault = 256;
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();  // clear the sticky error of a host without devices
+        return kDefault;
+    }
+    if (dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = kDefault;
+    }
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace fa
 
 extern "C" {
 

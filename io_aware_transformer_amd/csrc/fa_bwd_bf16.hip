@@ -35,13 +35,6 @@
 
 #include <type_traits>
 
-#ifndef FA_BWD_DKDV3
-#define FA_BWD_DKDV3 1
-#endif
-#ifndef FA_BWD_DKDV3_D64
-#define FA_BWD_DKDV3_D64 0
-#endif
-
 namespace fa {
 
 size_t bwd_workspace_bytes(int Hq, long long rows) {
@@ -86,12 +79,9 @@ template <>
 struct DkCfg<64> {
     static constexpr int KPW = 2;
 };
-#ifndef FA_BWD_KPW128
-#define FA_BWD_KPW128 1
-#endif
 template <>
 struct DkCfg<128> {
-    static constexpr int KPW = FA_BWD_KPW128;
+    static constexpr int KPW = 1;
 };
 constexpr int kDkWaves = 4;
 constexpr int kDkBQ = 64;
@@ -874,15 +864,6 @@ void bwd_dq2_kernel(BwdParams p) {
     }
 }
 
-template <typename K>
-hipError_t set_lds(K kern, size_t bytes, bool& done) {
-    if (done) return hipSuccess;
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
-    if (e == hipSuccess) done = true;
-    return e;
-}
-
 template <int D, int MASK>
 hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     // 1. D_i = dO_i . O_i
@@ -895,11 +876,11 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     if (e != hipSuccess) return e;
 
     // 2. dK, dV
-    if (FA_BWD_DKDV3 && (D == 128 || FA_BWD_DKDV3_D64)) {
+    if constexpr (D == 128) {
         auto kern = bwd_dkdv3_kernel<D, MASK>;
         constexpr size_t lds = Dk3Lds<D>::BYTES;
-        static bool attr = false;
-        if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
+        static DeviceOnce attr;
+        if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
         p.nkb = (p.N + kDk3KeysPerWg - 1) / kDk3KeysPerWg;
         const long long blocks = (long long)p.nkb * p.B * p.Hkv;
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
@@ -907,8 +888,8 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     } else {
         auto kern = bwd_dkdv2_kernel<D, MASK>;
         constexpr size_t lds = DkLds<D>::BYTES;
-        static bool attr = false;
-        if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
+        static DeviceOnce attr;
+        if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
         p.nkb = (p.N + dk_keys_per_wg<D>() - 1) / dk_keys_per_wg<D>();
         const long long blocks = (long long)p.nkb * p.B * p.Hkv;
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
@@ -918,8 +899,8 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     {
         auto kern = bwd_dq2_kernel<D, MASK>;
         constexpr size_t lds = DqLds<D>::BYTES;
-        static bool attr = false;
-        if ((e = set_lds(kern, lds, attr)) != hipSuccess) return e;
+        static DeviceOnce attr;
+        if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
         p.nqb = (p.N + kDqBM - 1) / kDqBM;
         const long long blocks = (long long)p.nqb * p.B * p.Hq;
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDqWaves * 64), lds, stream, p);

@@ -684,13 +684,9 @@ template <int D, int MASK>
 hipError_t launch_fwd_pp_t(FwdParams p, hipStream_t stream) {
     auto kern = fwd_pp_kernel<D, MASK>;
     constexpr size_t lds = pp_lds_bytes<D>();
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static DeviceOnce attr;
+    const hipError_t e = set_max_dynamic_lds(kern, lds, attr);
+    if (e != hipSuccess) return e;
     p.nqb = (p.N + kPPBM - 1) / kPPBM;
     const long long blocks = (long long)p.nqb * p.B * p.Hq;
     hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kPPWaves * 64), lds, stream, p);
@@ -701,13 +697,9 @@ template <int D, int MASK>
 hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
     auto kern = fwd_bf16_kernel<D, MASK>;
     constexpr size_t lds = fwd_lds_bytes<D>();
-    static bool attr_set = false;  // benign race: setting it twice is harmless
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static DeviceOnce attr;
+    const hipError_t e = set_max_dynamic_lds(kern, lds, attr);
+    if (e != hipSuccess) return e;
     constexpr int BM = fwd_bm<D>();
     p.nqb = (p.N + BM - 1) / BM;
     const long long blocks = (long long)p.nqb * p.B * p.Hq;

@@ -4,6 +4,9 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
+
+#include <atomic>
 
 namespace fa {
 
@@ -94,5 +97,22 @@ hipError_t launch_lse_merge(const float* Opart, const float* LSEpart, int parts,
 int split_parts_default(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 int split_chunk(int Nk, int parts);
 size_t split_workspace_bytes(int B, int Hq, int Nq, int d, int parts);
+
+// Host state shared by every call: per-device flags and a per-device cache
+// of the compute-unit count, both filled once and safe to use from several
+// host threads at once (atomics; a race only repeats an idempotent call).
+struct DeviceOnce {
+    std::atomic<uint64_t> done{0};  // bit i: set on device i
+};
+// Raises the dynamic-LDS limit of `kern` to `bytes` on the current device,
+// once per device.
+hipError_t set_max_dynamic_lds(const void* kern, size_t bytes, DeviceOnce& once);
+template <typename K>
+hipError_t set_max_dynamic_lds(K kern, size_t bytes, DeviceOnce& once) {
+    return set_max_dynamic_lds(reinterpret_cast<const void*>(kern), bytes, once);
+}
+// Compute units of the current device (256 on an MI355X; 256 as well when no
+// device can be queried, so host-only size queries stay defined).
+int device_cu_count();
 
 }  // namespace fa

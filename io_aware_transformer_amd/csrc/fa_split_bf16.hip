@@ -300,21 +300,12 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* _
     if (t == 0 && LSE != nullptr) LSE[row] = tot > 0.f ? M + logf(tot) : -INFINITY;
 }
 
-template <typename K>
-hipError_t set_lds_attr(K kern, size_t bytes, bool& done) {
-    if (done) return hipSuccess;
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
-    if (e == hipSuccess) done = true;
-    return e;
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch_split_t(SplitParams p, hipStream_t stream) {
     auto kern = fwd_split_kernel<D, CAUSAL>;
     constexpr size_t lds = split_lds_bytes<D>();
-    static bool attr = false;
-    hipError_t e = set_lds_attr(kern, lds, attr);
+    static DeviceOnce attr;
+    hipError_t e = set_max_dynamic_lds(kern, lds, attr);
     if (e != hipSuccess) return e;
     constexpr int NW = SplitCfg<D>::WAVES;
     const long long blocks = (long long)p.B * p.Hkv * p.nrb * ((p.parts + NW - 1) / NW);
@@ -342,12 +333,12 @@ int split_chunk(int Nk, int parts) {
 }
 
 int split_parts_default(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
-    // One workgroup per compute unit (256 of them, SplitCfg waves each: the
-    // LDS holds one), with at least four 32-key tiles per part.
+    // One workgroup per compute unit (SplitCfg waves each: the LDS holds
+    // one), with at least four 32-key tiles per part.
     const int nw = d == 64 ? SplitCfg<64>::WAVES : SplitCfg<128>::WAVES;
     const long long rows = (long long)(Hq / Hkv) * Nq;
     const long long waves = (long long)B * Hkv * ((rows + 31) / 32);
-    long long parts = (256LL * nw + waves - 1) / waves;
+    long long parts = ((long long)device_cu_count() * nw + waves - 1) / waves;
     const long long max_parts = ((long long)Nk + 4 * kSplitBN - 1) / (4 * kSplitBN);
     if (parts > max_parts) parts = max_parts;
     if (parts < 1) parts = 1;

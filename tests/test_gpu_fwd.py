@@ -62,8 +62,9 @@ def test_fwd_other_scales(scale):
 
 @pytest.mark.parametrize("name", ["c2", "c3a", "c3b", "c4a", "c4b", "c4c", "c5"])
 def test_fwd_preset_sampled_rows(name):
-    """Full-size presets: sampled rows of a few heads against the oracle's
-    row-by-row forward, plus properties that hold for every row."""
+    """Full-size presets: complete O / LSE of two heads and sampled rows of a
+    third (every query-block edge of 32, 64, 128 and 256 rows among them)
+    against the oracle, plus properties that hold for every row."""
     require_gpu()
     p = inputs.PRESETS[name]
     q, k, v = inputs.make_preset(p, with_grad=False)
@@ -76,9 +77,17 @@ def test_fwd_preset_sampled_rows(name):
     Q, K, V = f32np(q), f32np(k), f32np(v)
     rng = np.random.default_rng(p.seed)
     units = {(0, 0), (p.B - 1, p.Hq - 1), (int(rng.integers(p.B)), int(rng.integers(p.Hq)))}
-    edge = [0, 1, 31, 32, 63, 64, 127, 128, 129, p.N // 2, p.N - 2, p.N - 1]
+    edge = [0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, 257, 511, 512, 513, p.N // 2, p.N - 257, p.N - 256,
+            p.N - 2, p.N - 1]
     rows = sorted(set(edge + [int(x) for x in rng.integers(0, p.N, 20)]))
     tol = TOL[p.torch_dtype]
+    G = p.Hq // p.Hkv
+    for b, h in sorted(units)[:2]:
+        O, LSE = oracle.head_forward(Q[b, h].astype(np.float64), K[b, h // G].astype(np.float64),
+                                     V[b, h // G].astype(np.float64), p.scale, p.causal)
+        eo, el = maxabs(of[b, h], O), maxabs(lf[b, h], LSE)
+        assert eo <= tol["out"], ("complete head", b, h, eo)
+        assert el <= tol["lse"], ("complete head", b, h, el)
     for b, h in sorted(units):
         O, LSE = oracle.attention_forward_rows(Q, K, V, p.scale, p.causal, b, h, rows)
         eo = maxabs(of[b, h, rows], O)
