@@ -83,6 +83,8 @@ enum fa_status {
 /* Largest number of key ranges (partial results) of the split forward and
  * of the merge. */
 #define FA_MAX_SPLITS 4096
+/* Largest B * H_q * N of fa_bwd_noalloc (8 MiB of float32 D_i terms). */
+#define FA_NOALLOC_MAX_ROWS (1 << 21)
 
 /*
  * fa_fwd -- forward pass.
@@ -133,6 +135,25 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            void* workspace, size_t workspace_bytes,
            int B, int H_q, int H_kv, int N, int d, float scale, int causal,
            int dtype, void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, result and errors as fa_bwd, without the
+ * workspace: the D_i term goes to a fixed buffer inside the library (one
+ * per device, FA_NOALLOC_MAX_ROWS floats, kept until the process ends).
+ * Nothing is allocated or freed by the call.  Sizes with
+ * B * H_q * N > FA_NOALLOC_MAX_ROWS return FA_ERR_WORKSPACE (use
+ * fa_bwd).  Calls on one device share that buffer: calls that may overlap
+ * in time on one device (different streams, or different host threads
+ * without ordering) race and give unspecified gradients; calls ordered on
+ * one stream are safe.  The buffer's contents are rewritten before use, so
+ * nothing carries over between calls.
+ */
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                   int B, int H_q, int H_kv, int N, int d, float scale, int causal,
+                   int dtype, void* stream);
 
 /*
  * Local (sliding-window) attention.  The pages name local and sparse

@@ -9,6 +9,9 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
+# include/fa.h: largest B * H_q * N of fa_bwd_noalloc
+FA_NOALLOC_MAX_ROWS = 1 << 21
+
 # enum fa_dtype
 FA_BF16 = 0
 FA_FP32 = 1
@@ -45,6 +48,7 @@ EXPORTS = (
     "fa_fwd_varlen",
     "fa_bwd_varlen_workspace_size",
     "fa_bwd_varlen",
+    "fa_bwd_noalloc",
 )
 
 
@@ -110,6 +114,9 @@ def load():
     # Q K V O dO LSE dQ dK dV workspace | bytes | cu | batch total max_seqlen H_q H_kv d | scale | causal dtype | stream
     lib.fa_bwd_varlen.argtypes = [_vp] * 10 + [ctypes.c_size_t, _vp] + [_i] * 6 + [_f, _i, _i, _vp]
     lib.fa_bwd_varlen.restype = _i
+    # Q K V O dO LSE dQ dK dV | B H_q H_kv N d | scale | causal dtype | stream
+    lib.fa_bwd_noalloc.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp]
+    lib.fa_bwd_noalloc.restype = _i
     _lib = lib
     return lib
 

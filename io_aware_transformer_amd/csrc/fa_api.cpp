@@ -247,6 +247,23 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
                     causal ? -1 : -2, causal ? 0 : -2, dtype, stream);
 }
 
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                   void* dQ, void* dK, void* dV, int B, int H_q, int H_kv, int N, int d, float scale, int causal,
+                   int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    if (dtype == FA_BF16 && d == 256) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || N == 0) return FA_OK;
+    static_assert(fa::kNoAllocScratchBytes == size_t(FA_NOALLOC_MAX_ROWS) * sizeof(float), "limit and buffer agree");
+    if ((long long)B * H_q * N > (long long)FA_NOALLOC_MAX_ROWS) return FA_ERR_WORKSPACE;
+    if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
+    hipError_t e = hipSuccess;
+    void* scratch = fa::noalloc_scratch(e);
+    if (scratch == nullptr) return hip_failure(e);
+    return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, scratch, fa::kNoAllocScratchBytes, B, H_q, H_kv, N, d, scale,
+                    causal ? -1 : -2, causal ? 0 : -2, dtype, stream);
+}
+
 int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
                   void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv,
                   int N, int d, float scale, int window_left, int window_right, int dtype, void* stream) {

@@ -42,6 +42,32 @@ size_t bwd_workspace_bytes(int Hq, long long rows) {
     return (d_bytes + 255) / 256 * 256;
 }
 
+// Fixed device buffer of the allocation-free backward (fa_bwd_noalloc): it
+// holds the D_i term in place of a caller workspace.  Every device the
+// library runs on keeps one copy for the life of the process; calls on one
+// device share it (and race when they overlap).
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch(hipError_t& err) {
+    // The host-side name `scratch` is only a handle: its device address,
+    // different on every device, comes from hipGetSymbolAddress, taken once
+    // per device with that device current.
+    static std::atomic<void*> addr[64];
+    int dev = 0;
+    err = hipGetDevice(&dev);
+    if (err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= 64) {
+        err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    void* ptr = addr[dev].load(std::memory_order_acquire);
+    if (ptr != nullptr) return ptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return nullptr;
+    addr[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+
 namespace {
 
 // ---------------------------------------------------------------- bwd_pre

@@ -88,6 +88,12 @@ hipError_t launch_bwd_f32(BwdParams p, int d, int causal, hipStream_t stream);
 // sequences): the D term only.
 size_t bwd_workspace_bytes(int Hq, long long rows);
 
+// Allocation-free backward: size of the fixed per-device buffer that holds
+// the D_i term (float [B, Hq, N] rows, 256-byte aligned), and its device
+// address on the current device (nullptr and `err` set on failure).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+void* noalloc_scratch(hipError_t& err);
+
 // Split forward: partial kernel (launch_fwd_split_bf16, d in {64, 128}) and
 // the merge of partials (launch_lse_merge, d in {64, 128, 256}, output bf16
 // when out_bf16 else float32).

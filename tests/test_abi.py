@@ -328,3 +328,40 @@ def test_varlen_empty_is_noop():
     gnone = dict(none, dO=None, dQ=None, dK=None, dV=None, ws=None)
     assert bwdv(batch=0, **gnone) == 0
     assert bwdv(total=0, **gnone) == 0
+
+
+def bwdn(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, LSE=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE,
+             B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125, causal=1, dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_bwd_noalloc(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"],
+                                      a["dV"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"],
+                                      a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), "FA_ERR_NULL"),
+    (dict(dV=None), "FA_ERR_NULL"),
+    (dict(Hq=3, Hkv=2), "FA_ERR_SHAPE"),
+    (dict(d=96), "FA_ERR_HEADDIM"),
+    (dict(d=256), "FA_ERR_UNSUPPORTED"),
+    (dict(causal=2), "FA_ERR_ARG"),
+    (dict(scale=float("inf")), "FA_ERR_ARG"),
+    (dict(dtype=7), "FA_ERR_DTYPE"),
+    # the fixed buffer holds FA_NOALLOC_MAX_ROWS rows of D_i
+    (dict(B=1, Hq=16, Hkv=16, N=_lib.FA_NOALLOC_MAX_ROWS // 16 + 1), "FA_ERR_WORKSPACE"),
+    (dict(B=2, Hq=1, Hkv=1, N=_lib.FA_NOALLOC_MAX_ROWS // 2 + 1), "FA_ERR_WORKSPACE"),
+])
+def test_bwd_noalloc_rejects(kw, code):
+    assert bwdn(**kw) == E[code]
+
+
+def test_bwd_noalloc_empty_is_noop():
+    assert bwdn(B=0, Q=None) == E["FA_OK"]
+    assert bwdn(N=0, Q=None) == E["FA_OK"]
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_MAX_ROWS \(1 << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == _lib.FA_NOALLOC_MAX_ROWS
