@@ -355,41 +355,36 @@ void fwd_bf16_kernel(FwdParams p) {
 //   M phase j:  O^T += V_{j-1}^T P_{j-1}^T   and   S_j^T = K_j Q^T   (MFMA)
 //   V phase j:  softmax of S_j (max, rescale, exp2, sum, bf16 P_j)   (VALU)
 // While group A is in an M phase, group B is in a V phase and vice versa;
-// a workgroup barrier closes every phase and keeps the offset.  K/V tiles
-// are triple-buffered in LDS: tile j is read from A's M phase j to B's M
-// phase j+1, and tile j+3 is copied into its buffer two phases before it is
-// first needed.  Group A owns query rows q0 .. q0+127, group B q0+128 ..
-// q0+255.
+// a workgroup barrier closes every phase and keeps the offset.  The V^T
+// operand of O^T += V^T P^T is read straight from the row-major V tile with
+// transposing LDS reads (ds_read_b64_tr_b16), so both groups' V phases are
+// the softmax alone.  K/V tiles go through four LDS stages: tile t is read
+// from A's M phase t to B's M phase t+1, and is copied into the stage of
+// tile t-4 at step 2t-4, four phases before its first use; each wave waits
+// only for its own copies of the tile about to be read (the newer tile may
+// stay in flight).  Group A owns query rows q0 .. q0+127, group B
+// q0+128 .. q0+255.
 // ---------------------------------------------------------------------------
-template <int D>
-struct PPCfg;
-template <>
-struct PPCfg<64> {
-    static constexpr int BN = FA_FWD_BN64;
-};
-template <>
-struct PPCfg<128> {
-    static constexpr int BN = FA_FWD_BN128;
-};
 constexpr int kPPWaves = 8;
-constexpr int kPPStages = 3;
+constexpr int kPPStages = 4;
 constexpr int kPPBM = 32 * kPPWaves;
+constexpr int kPPBN = 64;
 
 template <int D>
 constexpr size_t pp_lds_bytes() {
-    // K/V stages plus two V^T buffers
-    return (size_t(kPPStages) * 2 + 2) * PPCfg<D>::BN * D * sizeof(bf16);
+    return size_t(kPPStages) * 2 * kPPBN * D * sizeof(bf16);
 }
 
-// V^T tile layout: element (dim, key) of a D x BN tile.  Keys are grouped
-// by 16; inside a group the order is [4hi+0..3, 8+4hi+0..3] for hi = 0, 1,
-// which is the key order of the MFMA A operand, so one 16-byte read gives a
-// lane its 8 keys; the two 16-byte halves of a row are swapped when bit 3
-// of the dim is set (conflict-free reads of 16 consecutive dims).
-template <int D>
-__device__ __forceinline__ int vt_off(int dim, int key) {
-    return (key >> 4) * D * 16 + dim * 16 + 8 * (((key >> 2) & 1) ^ ((dim >> 3) & 1)) + 4 * ((key >> 3) & 1) +
-           (key & 3);
+// s_waitcnt vmcnt(n) for a wave-uniform n known only at run time: the
+// count is an immediate, so dispatch over the values the kernel uses.
+template <int STEP>
+__device__ __forceinline__ void wait_vmem_at_most(int n_groups) {
+    switch (n_groups) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F70 | (1 * STEP)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * STEP)); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * STEP)); break;
+    }
 }
 
 template <int D, int MASK>
@@ -401,11 +396,14 @@ void fwd_pp_kernel(FwdParams p) {
     constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
     const int wl_ = MASK == 2 ? p.wl : kUnbounded;
     const int wr_ = MASK == 2 ? p.wr : 0;
-    constexpr int BN = PPCfg<D>::BN;
+    constexpr int BN = kPPBN;
     constexpr int NST = kPPStages;
     constexpr int BM = kPPBM;
     constexpr int TILE = BN * D;
     constexpr int KB = BN / 32;
+    using Copy = TileCopy<D, BN, kPPWaves>;
+    constexpr int CPW = 2 * Copy::PER_WAVE;  // copy instructions per wave per tile
+    static_assert(CPW * 3 < 16, "vmcnt immediates stay in the low field");
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
     bf16* smem = reinterpret_cast<bf16*>(smem_raw);
 
@@ -439,12 +437,8 @@ void fwd_pp_kernel(FwdParams p) {
     const int kt0 = WIN ? max(0, q0 - wl_) / BN : 0;
     const int T = (kend + BN - 1) / BN - kt0;
 
-    TileCopy<D, BN, kPPWaves> cp;
-    cp.init(w, lane);
-#pragma unroll
-    for (int t = 0; t < NST; ++t)
-        if (t < T) cp.issue(Kh, Vh, smem + t * 2 * TILE, smem + t * 2 * TILE + TILE, (kt0 + t) * BN, N);
-
+    // Q rows first (the oldest loads of the wave), then the prologue tiles
+    // 0 .. min(T, NST) - 1 into the empty stages.
     bf16x8 qreg[D / 16];
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc) {
@@ -453,6 +447,11 @@ void fwd_pp_kernel(FwdParams p) {
         if (p.qmode == 1) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
         qreg[cc] = as_bf16x8(v);
     }
+    Copy cp;
+    cp.init(w, lane);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+        if (t < T) cp.issue(Kh, Vh, smem + t * 2 * TILE, smem + t * 2 * TILE + TILE, (kt0 + t) * BN, N);
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -466,6 +465,8 @@ void fwd_pp_kernel(FwdParams p) {
     // Finite floor for the running max: a row whose first tiles are all
     // masked (left window edge) keeps exp2(m_old - m_new) defined.
     float m = -3.0e38f, l = 0.f;
+    // Transposing reads of the V operand: lane (4e + i) of each 16-lane
+    // group addresses key row e (+ 4hi) of a 16-key block, 4 dims at tcol.
     const int trow = 4 * hi + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int key_lim = CAUSAL ? min(qrow + wr_, N - 1) : N - 1;  // last visible key of this row
@@ -479,48 +480,34 @@ void fwd_pp_kernel(FwdParams p) {
         return min(KB, (wq_last + wr_ - kstart) / 32 + 1);
     };
 
-    wait_vmem();
+    // Tile 0 must be in LDS before step 0: wait for it (the newer prologue
+    // tiles may stay in flight), then publish.
+    wait_vmem_at_most<CPW>(min(T, NST) - 1);
     __syncthreads();
-
-    // Per-lane element offset of the V^T A-operand read (dim l32 of a 32-dim
-    // block, the 8 keys of half hi of a 16-key group).
-    const int vt_lane = vt_off<D>(l32, 4 * hi);
-    // Transpose tile j's V (V slabs) into V^T buffer j % 2.  Done by the 4
-    // waves of group A in their V phase; each transposing read returns 4
-    // consecutive keys of one dim, written back as one 8-byte store.
-    constexpr int TR_PER_WAVE = (BN / 8) * (D / 32) / 4;
-    auto transpose_v = [&](int j, bf16x4 (&buf)[TR_PER_WAVE], bool write) {
-        const bf16* Vs = smem + (j % NST) * 2 * TILE + TILE;
-        bf16* VT = smem + (2 * NST + (j & 1)) * TILE;
-#pragma unroll
-        for (int i = 0; i < TR_PER_WAVE; ++i) {
-            const int t = w + 4 * i;  // instruction index 0 .. (BN/8)(D/32) - 1
-            const int kb8 = t / (D / 32), db = t - (t / (D / 32)) * (D / 32);
-            if (!write) {
-                buf[i] = lds_read_tr(Vs + vslab_off<BN>(8 * kb8 + trow, db * 32 + tcol));
-            } else {
-                *reinterpret_cast<bf16x4*>(VT + vt_off<D>(db * 32 + l32, 8 * kb8 + 4 * hi)) = buf[i];
-            }
-        }
-    };
 
     // Steps 0 .. 2T+1, one workgroup barrier after each.  Group A: step 2j is
     // its M phase j, step 2j+1 its V phase j.  Group B runs one step later.
-    // K/V refill: at even step 2t-2 (t >= 3) tile t goes into the buffer of
-    // tile t-3, whose last reader (group B, M phase t-2) finished in the
-    // previous step; the copy is waited for at the end of the next (odd) step.
+    // Refill: at even step 2u (u >= 2) tile u + 2 goes into the stage of
+    // tile u - 2, whose last reader (group B, M phase u - 1: the V operand
+    // of tile u - 2) finished at the previous barrier.
     auto refill = [&](int step) {
         if (!(step & 1) && step >= 4) {
-            const int t = step / 2 + 1;
+            const int t = step / 2 + 2;
             if (t < T) {
                 bf16* st = smem + (t % NST) * 2 * TILE;
                 cp.issue(Kh, Vh, st, st + TILE, (kt0 + t) * BN, N);
             }
         }
     };
+    // End of a step: before step 2t (group A reads K_t) every wave has
+    // waited for its own copies of tile t.  At the end of step 2t - 1 the
+    // tiles issued so far are 0 .. max(NST - 1, t + 1) (bounded by T - 1).
     auto finish = [&](int step) {
-        if ((step & 1) && step >= 5) wait_vmem();
-        wait_lds();  // this wave's LDS writes are done
+        if (step & 1) {
+            const int t = (step + 1) / 2;
+            if (t < T) wait_vmem_at_most<CPW>(min(T - 1, max(NST - 1, t + 1)) - t);
+        }
+        wait_lds();  // this wave's LDS reads are done before the stage can be refilled
         __builtin_amdgcn_s_barrier();
     };
     // ---- M phase j: PV of tile j-1, then QK of tile j.  LDS fragments are
@@ -528,25 +515,29 @@ void fwd_pp_kernel(FwdParams p) {
     // keep at most two blocks live.
     auto phase_m = [&](int j) {
         if (j >= 1 && active_kb(j - 1) > 0) {
-            // V^T of tile j-1 (written by group A in its V phase j-1): one
-            // 16-byte read per A operand.
-            const bf16* VT = smem + (2 * NST + ((j - 1) & 1)) * TILE + vt_lane;
+            // V^T A operand of contraction block (kb, cc): keys
+            // 32kb + 16cc + 8(sl/4) + 4hi + sl%4 of dims db*32 + l32, read
+            // transposed from the V slabs of tile j-1.
+            const bf16* Vs = smem + ((j - 1) % NST) * 2 * TILE + TILE;
             bf16x8 fa[D / 32], fb[D / 32];
+            auto load_v = [&](bf16x8(&f)[D / 32], int kb, int cc) {
+                const int key = kb * 32 + 16 * cc + trow;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) fa[db] = as_bf16x8(ld16(VT + db * 32 * 16));
+                for (int db = 0; db < D / 32; ++db) {
+                    const bf16x4 v0 = lds_read_tr(Vs + vslab_off<BN>(key, db * 32 + tcol));
+                    const bf16x4 v1 = lds_read_tr(Vs + vslab_off<BN>(key + 8, db * 32 + tcol));
+                    f[db] = cat(v0, v1);
+                }
+            };
+            load_v(fa, 0, 0);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) fb[db] = as_bf16x8(ld16(VT + (2 * kb + 1) * D * 16 + db * 32 * 16));
+                load_v(fb, kb, 1);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x16(fa[db], pb[kb][0], o[db]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (kb + 1 < KB) {
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db)
-                        fa[db] = as_bf16x8(ld16(VT + (2 * kb + 2) * D * 16 + db * 32 * 16));
-                }
+                if (kb + 1 < KB) load_v(fa, kb + 1, 0);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x16(fb[db], pb[kb][1], o[db]);
@@ -559,13 +550,13 @@ void fwd_pp_kernel(FwdParams p) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 s[kb] = f32x16{};
-                ka[kb] = as_bf16x8(ld16(Ks + kslab_off<BN>(kb * 32 + l32, 8 * hi)));
+                ka[kb] = as_bf16x8(lds16(Ks + kslab_off<BN>(kb * 32 + l32, 8 * hi)));
             }
 #pragma unroll
             for (int cc = 0; cc < D / 16; cc += 2) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
-                    kbf[kb] = as_bf16x8(ld16(Ks + kslab_off<BN>(kb * 32 + l32, 16 * (cc + 1) + 8 * hi)));
+                    kbf[kb] = as_bf16x8(lds16(Ks + kslab_off<BN>(kb * 32 + l32, 16 * (cc + 1) + 8 * hi)));
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) s[kb] = mfma_32x32x16(ka[kb], qreg[cc], s[kb]);
@@ -573,7 +564,7 @@ void fwd_pp_kernel(FwdParams p) {
                 if (cc + 2 < D / 16) {
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
-                        ka[kb] = as_bf16x8(ld16(Ks + kslab_off<BN>(kb * 32 + l32, 16 * (cc + 2) + 8 * hi)));
+                        ka[kb] = as_bf16x8(lds16(Ks + kslab_off<BN>(kb * 32 + l32, 16 * (cc + 2) + 8 * hi)));
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -641,12 +632,7 @@ void fwd_pp_kernel(FwdParams p) {
             phase_m(j);
             finish(2 * j);
             refill(2 * j + 1);
-            if (j < T) {
-                bf16x4 tb[TR_PER_WAVE];
-                transpose_v(j, tb, false);
-                phase_v(j);
-                transpose_v(j, tb, true);
-            }
+            phase_v(j);
             finish(2 * j + 1);
         }
     } else {
