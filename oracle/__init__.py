@@ -11,12 +11,13 @@ matrix, stable row softmax, multiply by V) and the textbook analytic
 backward, in float64, one (batch, query-head) unit at a time, plus
 attention with queries and keys of different lengths, attention over a key
 range, the merge of partial results over disjoint key ranges, local
-(sliding-window) attention and batches of packed sequences of different
-lengths.  Every function cites the passage of the source pages it follows;
+(sliding-window) attention, batches of packed sequences of different
+lengths and block-sparse attention.  Every function cites the passage of the source pages it follows;
 see ``oracle/attention.py``, ``oracle/splitkv.py``, ``oracle/window.py`` and
-``oracle/varlen.py``.
+``oracle/varlen.py`` and ``oracle/blocksparse.py``.
 """
 
+from .blocksparse import blocksparse_backward, blocksparse_forward, blocksparse_visible
 from .attention import (
     attention_forward,
     attention_backward,
@@ -44,4 +45,7 @@ __all__ = [
     "window_visible",
     "varlen_forward",
     "varlen_backward",
+    "blocksparse_forward",
+    "blocksparse_backward",
+    "blocksparse_visible",
 ]

@@ -17,6 +17,7 @@ import os
 import numpy as np
 
 import oracle.attention as OA
+import oracle.blocksparse as OB
 import oracle.splitkv as OS
 import oracle.varlen as OV
 import oracle.window as OW
@@ -574,6 +575,126 @@ def check_varlen_finite_differences(seed=26):
                 assert abs(fd - Gr[ix]) < 1e-7 * max(1.0, abs(fd)), (ix, fd, Gr[ix])
 
 
+# ---------------------------------------------------------------- block-sparse masks
+
+
+def _bs_mask(rng, nb, density):
+    return (rng.random((nb, nb)) < density).astype(np.uint8)
+
+
+def check_blocksparse_full_and_causal_maps(seed=41):
+    """An all-ones map is plain attention (causal or not); a lower-triangular
+    map with causal is the causal mask; forward and backward.  N = 300 spans
+    three 128-blocks with a ragged last one."""
+    rng = np.random.default_rng(seed)
+    n = 300
+    nb = 3
+    Q, K, V = _qkv(rng, 1, 2, 1, n, n, 4)
+    dO = rng.standard_normal(Q.shape)
+    ones = np.ones((nb, nb), dtype=np.uint8)
+    tril = np.tril(ones)
+    for mask, causal in ((ones, False), (ones, True), (tril, True)):
+        O, L = OB.blocksparse_forward(Q, K, V, mask, 0.3, causal)
+        Or, Lr = OA.attention_forward(Q, K, V, 0.3, causal)
+        assert np.max(np.abs(O - Or)) < 1e-13 and np.max(np.abs(L - Lr)) < 1e-12
+        g = OB.blocksparse_backward(Q, K, V, dO, mask, 0.3, causal)
+        gr = OA.attention_backward(Q, K, V, dO, 0.3, causal)
+        for a, b in zip(g, gr):
+            assert np.max(np.abs(a - b)) < 1e-11
+
+
+def check_blocksparse_block_diagonal(seed=42):
+    """A block-diagonal map is independent attention inside every 128-block
+    (the square definition on each slice, the last one ragged)."""
+    rng = np.random.default_rng(seed)
+    n = 290
+    Q, K, V = _qkv(rng, 2, 2, 2, n, n, 3)
+    mask = np.eye(3, dtype=np.uint8)
+    for causal in (False, True):
+        O, L = OB.blocksparse_forward(Q, K, V, mask, 0.5, causal)
+        for b in range(2):
+            for h in range(2):
+                for a in range(0, n, OB.BLOCK):
+                    e = min(n, a + OB.BLOCK)
+                    o, l = OA.head_forward(Q[b, h, a:e], K[b, h, a:e], V[b, h, a:e], 0.5, causal)
+                    assert np.max(np.abs(O[b, h, a:e] - o)) < 1e-13
+                    assert np.max(np.abs(L[b, h, a:e] - l)) < 1e-12
+
+
+def check_blocksparse_rows_are_gathers(seed=43):
+    """Row i of a random map is the square definition of query i over the
+    keys it sees, gathered (not masked) from K and V."""
+    rng = np.random.default_rng(seed)
+    n = 260
+    Q, K, V = _qkv(rng, 1, 1, 1, n, n, 5)
+    mask = _bs_mask(rng, 3, 0.6)
+    mask[0, 0] = 1  # causal rows of block 0 then see at least their block
+    for causal in (False, True):
+        O, L = OB.blocksparse_forward(Q, K, V, mask, 0.7, causal)
+        for i in range(0, n, 7):
+            keys = [j for j in range(n) if mask[i // 128, j // 128] and (not causal or j <= i)]
+            if not keys:
+                assert np.all(O[0, 0, i] == 0) and L[0, 0, i] == -np.inf
+                continue
+            o, l = OA.head_forward(Q[0, 0, i:i + 1], K[0, 0, keys], V[0, 0, keys], 0.7, False)
+            assert np.max(np.abs(O[0, 0, i] - o[0])) < 1e-13 and abs(L[0, 0, i] - l[0]) < 1e-12
+
+
+def check_blocksparse_empty_rows(seed=44):
+    """Query blocks whose map row is all zero see nothing: O = 0, LSE = -inf,
+    dQ = 0 there, and the other rows and every dK / dV equal the same
+    problem without those queries (they add no gradient)."""
+    rng = np.random.default_rng(seed)
+    n = 300
+    Q, K, V = _qkv(rng, 1, 2, 1, n, n, 4)
+    dO = rng.standard_normal(Q.shape)
+    mask = np.array([[1, 0, 1], [0, 0, 0], [1, 1, 1]], dtype=np.uint8)
+    O, L = OB.blocksparse_forward(Q, K, V, mask, 0.4, False)
+    dQ, dK, dV = OB.blocksparse_backward(Q, K, V, dO, mask, 0.4, False)
+    hid = slice(128, 256)
+    assert np.all(O[:, :, hid] == 0) and np.all(L[:, :, hid] == -np.inf) and np.all(dQ[:, :, hid] == 0)
+    keep = np.r_[0:128, 256:300]
+    vis = OB.blocksparse_visible(n, mask, False)[keep]
+    dKr, dVr = np.zeros_like(K), np.zeros_like(V)
+    for h in range(2):
+        s = np.where(vis, 0.4 * Q[0, h, keep] @ K[0, 0].T, -np.inf)
+        m = s.max(axis=1)
+        p = np.exp(s - m[:, None])
+        p /= p.sum(axis=1)[:, None]
+        assert np.max(np.abs(O[0, h, keep] - p @ V[0, 0])) < 1e-13
+        dp = dO[0, h, keep] @ V[0, 0].T
+        ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+        dKr[0, 0] += 0.4 * ds.T @ Q[0, h, keep]
+        dVr[0, 0] += p.T @ dO[0, h, keep]
+    assert np.max(np.abs(dK - dKr)) < 1e-12 and np.max(np.abs(dV - dVr)) < 1e-12
+
+
+def check_blocksparse_finite_differences(seed=45):
+    """Central differences of <dO, O> for a random map with causal, grouped
+    heads, a ragged last block and an empty query block."""
+    rng = np.random.default_rng(seed)
+    n = 140
+    Q, K, V = _qkv(rng, 1, 2, 1, n, n, 3)
+    dO = rng.standard_normal(Q.shape)
+    mask = np.array([[1, 0], [1, 1]], dtype=np.uint8)
+    sc, h = 0.9, 1e-6
+    for causal in (False, True):
+        dQ, dK, dV = OB.blocksparse_backward(Q, K, V, dO, mask, sc, causal)
+
+        def loss(q, k, v):
+            return float((OB.blocksparse_forward(q, k, v, mask, sc, causal)[0] * dO).sum())
+
+        for X, G in ((Q, dQ), (K, dK), (V, dV)):
+            for _ in range(5):
+                ix = tuple(int(rng.integers(0, s)) for s in X.shape)
+                Xp, Xm = X.copy(), X.copy()
+                Xp[ix] += h
+                Xm[ix] -= h
+                fd = (loss(*[Xp if Y is X else Y for Y in (Q, K, V)]) -
+                      loss(*[Xm if Y is X else Y for Y in (Q, K, V)])) / (2 * h)
+                assert abs(fd - G[ix]) < 1e-7 * max(1.0, abs(fd)), (ix, fd, G[ix])
+
+
 ALL_CHECKS = [
     check_four_token_tiles_consistent,
     check_four_token_recurrence_values,
@@ -599,4 +720,9 @@ ALL_CHECKS = [
     check_varlen_equal_lengths,
     check_varlen_ragged_slices,
     check_varlen_finite_differences,
+    check_blocksparse_full_and_causal_maps,
+    check_blocksparse_block_diagonal,
+    check_blocksparse_rows_are_gathers,
+    check_blocksparse_empty_rows,
+    check_blocksparse_finite_differences,
 ]

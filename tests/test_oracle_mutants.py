@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as OA
+import oracle.blocksparse as OB
 import oracle.splitkv as OS
 import oracle.varlen as OV
 import oracle.window as OW
@@ -233,6 +234,43 @@ def _varlen_bwd_overwrite(Q, K, V, dO, cu, scale, causal):
     return dQ, dK, dV
 
 
+def _bs_visible_transposed(n, mask, causal):
+    return OB_orig["blocksparse_visible"](n, np.asarray(mask).T, causal)
+
+
+def _bs_visible_block64(n, mask, causal):
+    mask = np.asarray(mask)
+    blk = np.minimum(np.arange(n) // 64, mask.shape[0] - 1)
+    vis = mask[blk[:, None], blk[None, :]] != 0
+    if causal:
+        vis &= np.arange(n)[None, :] <= np.arange(n)[:, None]
+    return vis
+
+
+def _bs_probs_empty_rows_see_all(q, k, scale, vis):
+    vis = np.where(vis.any(axis=1)[:, None], vis, True)
+    return OB_orig["_probs"](q, k, scale, vis)
+
+
+def _bs_bwd_no_rowterm(Q, K, V, dO, mask, scale, causal):
+    Q, K, V, dO = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, dO))
+    B, Hq, Hkv, N, d = OA._check_shapes(Q, K, V)
+    vis = OB.blocksparse_visible(N, mask, causal)
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = OA.kv_head_of(h, Hq, Hkv)
+            p, _ = OB._probs(Q[b, h], K[b, g], scale, vis)
+            ds = p * (dO[b, h] @ V[b, g].T)
+            dQ[b, h] = scale * (ds @ K[b, g])
+            dK[b, g] += scale * (ds.T @ Q[b, h])
+            dV[b, g] += p.T @ dO[b, h]
+    return dQ, dK, dV
+
+
+OB_orig = {"blocksparse_visible": OB.blocksparse_visible, "_probs": OB._probs}
+
+
 MUTANTS = {
     "scale_dropped": ("_scores", _scores_no_scale),
     "scale_twice": ("_scores", _scores_scale_twice),
@@ -262,6 +300,10 @@ MUTANTS = {
     "varlen_leaks_previous_sequence": (OV, "varlen_forward", _varlen_fwd_factory("leak_previous")),
     "varlen_kv_head_by_query_index": (OV, "varlen_forward", _varlen_fwd_factory("kv_head_by_query")),
     "varlen_group_grads_overwritten": (OV, "varlen_backward", _varlen_bwd_overwrite),
+    "blocksparse_map_transposed": (OB, "blocksparse_visible", _bs_visible_transposed),
+    "blocksparse_blocks_of_64": (OB, "blocksparse_visible", _bs_visible_block64),
+    "blocksparse_empty_rows_see_all": (OB, "_probs", _bs_probs_empty_rows_see_all),
+    "blocksparse_bwd_missing_row_term": (OB, "blocksparse_backward", _bs_bwd_no_rowterm),
 }
 
 
