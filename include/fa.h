@@ -83,6 +83,10 @@ enum fa_status {
 /* Largest number of key ranges (partial results) of the split forward and
  * of the merge. */
 #define FA_MAX_SPLITS 4096
+/* Block-sparse attention: positions per block of the block map, and the
+ * longest sequence its entry points accept. */
+#define FA_SPARSE_BLOCK 128
+#define FA_SPARSE_MAX_N 65536
 /* Largest B * H_q * N of fa_bwd_noalloc (8 MiB of float32 D_i terms). */
 #define FA_NOALLOC_MAX_ROWS (1 << 21)
 
@@ -180,6 +184,37 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O,
                   void* workspace, size_t workspace_bytes,
                   int B, int H_q, int H_kv, int N, int d, float scale,
                   int window_left, int window_right, int dtype, void* stream);
+
+/*
+ * Block-sparse attention.  The deep-dive page ("Flash attention: fast and
+ * memory-efficient exact attention with IO-awareness -- a deep dive") names
+ * block-sparse FlashAttention in its closing paragraph, and the interview
+ * Q&A (app.wittybyte.ai, "FlashAttention1", scaling answer) suggests sparse
+ * patterns for very long sequences; neither defines a layout.  Reading: the
+ * sequence is cut into blocks of FA_SPARSE_BLOCK = 128 positions; the map
+ *   block_mask  uint8 [nb][nb], nb = ceil(N / 128), DEVICE memory, one map
+ *               for every batch entry and head (nonzero = visible)
+ * lets query i see key j exactly when block_mask[i / 128][j / 128] != 0,
+ * and with causal = 1 also j <= i.  Key tiles of hidden blocks are neither
+ * loaded nor computed.  A query row that sees no key gets O = 0 and
+ * LSE = -inf and adds nothing to dK / dV; its dQ row is 0.
+ *
+ * fa_fwd_blocksparse / fa_bwd_blocksparse -- as fa_fwd / fa_bwd plus the
+ * map; fa_bwd_blocksparse must get O and LSE of fa_fwd_blocksparse with the
+ * same map, scale and causal flag (workspace: fa_bwd_workspace_size).
+ * FA_BF16 with d in {64, 128} and N <= FA_SPARSE_MAX_N; other valid
+ * combinations return FA_ERR_UNSUPPORTED.  block_mask NULL: FA_ERR_NULL.
+ * The host does not read the map (no synchronisation); it must hold nb * nb
+ * bytes.
+ */
+int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                       const unsigned char* block_mask, int B, int H_q, int H_kv, int N, int d,
+                       float scale, int causal, int dtype, void* stream);
+int fa_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O,
+                       const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                       void* workspace, size_t workspace_bytes, const unsigned char* block_mask,
+                       int B, int H_q, int H_kv, int N, int d, float scale, int causal,
+                       int dtype, void* stream);
 
 /*
  * Packed variable-length batches.  The interview Q&A page (app.wittybyte.ai,

@@ -9,6 +9,9 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
+# include/fa.h: block-sparse map blocks and sequence limit
+FA_SPARSE_BLOCK = 128
+FA_SPARSE_MAX_N = 65536
 # include/fa.h: largest B * H_q * N of fa_bwd_noalloc
 FA_NOALLOC_MAX_ROWS = 1 << 21
 
@@ -49,6 +52,8 @@ EXPORTS = (
     "fa_bwd_varlen_workspace_size",
     "fa_bwd_varlen",
     "fa_bwd_noalloc",
+    "fa_fwd_blocksparse",
+    "fa_bwd_blocksparse",
 )
 
 
@@ -117,6 +122,12 @@ def load():
     # Q K V O dO LSE dQ dK dV | B H_q H_kv N d | scale | causal dtype | stream
     lib.fa_bwd_noalloc.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp]
     lib.fa_bwd_noalloc.restype = _i
+    # Q K V O LSE mask | B H_q H_kv N d | scale | causal dtype | stream
+    lib.fa_fwd_blocksparse.argtypes = [_vp] * 6 + [_i] * 5 + [_f, _i, _i, _vp]
+    lib.fa_fwd_blocksparse.restype = _i
+    # Q K V O dO LSE dQ dK dV workspace | bytes | mask | B H_q H_kv N d | scale | causal dtype | stream
+    lib.fa_bwd_blocksparse.argtypes = [_vp] * 10 + [ctypes.c_size_t, _vp] + [_i] * 5 + [_f, _i, _i, _vp]
+    lib.fa_bwd_blocksparse.restype = _i
     _lib = lib
     return lib
 

@@ -292,3 +292,55 @@ def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, scale=None, causal=T
     )
     _lib.check(st, "fa_bwd_varlen")
     return dq, dk, dv
+
+
+def _check_block_mask(mask, N, device):
+    nb = (N + _lib.FA_SPARSE_BLOCK - 1) // _lib.FA_SPARSE_BLOCK
+    if mask.dtype not in (torch.uint8, torch.bool) or tuple(mask.shape) != (nb, nb):
+        raise ValueError(f"block_mask must be a uint8 or bool tensor of shape ({nb}, {nb}) for N = {N}")
+    if mask.device != device or not mask.is_contiguous():
+        raise ValueError("block_mask must be a contiguous tensor on the tensors' device")
+    return mask
+
+
+def fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False, out=None, lse=None):
+    """Block-sparse forward: query i sees key j when
+    block_mask[i // 128, j // 128] is nonzero (and j <= i with causal).
+    Rows that see nothing get o = 0, lse = -inf.  Returns (o, lse) as ``fwd``."""
+    B, Hq, Hkv, N, d = _check(q, k, v)
+    _check_block_mask(block_mask, N, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = _buffer(out, q.shape, q.dtype, q.device, "out")
+    lse = _buffer(lse, (B, Hq, N), torch.float32, q.device, "lse")
+    _on_device(q)
+    st = _lib.load().fa_fwd_blocksparse(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        lse.data_ptr() or None, block_mask.data_ptr() or None, B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+        _DTYPES[q.dtype], _stream(q.device),
+    )
+    _lib.check(st, "fa_fwd_blocksparse")
+    return o, lse
+
+
+def bwd_blocksparse(q, k, v, o, lse, do, block_mask, scale=None, causal=False, workspace=None):
+    """Backward of ``fwd_blocksparse`` with the same map: returns (dq, dk, dv)."""
+    B, Hq, Hkv, N, d = _check(q, k, v, o, do)
+    _check_block_mask(block_mask, N, q.device)
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H_q, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    _on_device(q)
+    st = _lib.load().fa_bwd_blocksparse(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        do.data_ptr() or None, lse.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,
+        dv.data_ptr() or None, workspace.data_ptr() or None, workspace.numel(), block_mask.data_ptr() or None,
+        B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype], _stream(q.device),
+    )
+    _lib.check(st, "fa_bwd_blocksparse")
+    return dq, dk, dv

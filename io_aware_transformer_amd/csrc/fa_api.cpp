@@ -74,7 +74,8 @@ bool window_bounds(int left, int right, int N, int& wl, int& wr) {
 // Fixed-length batches pass cu == nullptr; packed sequences pass the device
 // offsets, the packed row count `total` and the longest length as N.
 int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N, int d,
-             float scale, int left, int right, int dtype, void* stream, const int* cu = nullptr, int total = 0) {
+             float scale, int left, int right, int dtype, void* stream, const int* cu = nullptr, int total = 0,
+             const unsigned char* bmask = nullptr) {
     if (B == 0 || N == 0) return FA_OK;
     if (!Q || !K || !V || !O) return FA_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 16))
@@ -92,16 +93,23 @@ int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, i
     p.cu = cu;
     p.total = total;
     p.scale_log2 = scale * kLog2e;
-    const bool masked = window_bounds(left, right, N, p.wl, p.wr);
+    bool masked = window_bounds(left, right, N, p.wl, p.wr);
+    if (bmask != nullptr) {
+        p.bmask = bmask;
+        p.nb = (N + fa::kSparseBlock - 1) / fa::kSparseBlock;
+        masked = true;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = (dtype == FA_BF16) ? fa::launch_fwd_bf16(p, d, masked, s) : fa::launch_fwd_f32(p, d, masked, s);
+    if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
     if (e != hipSuccess) return hip_failure(e);
     return FA_OK;
 }
 
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
              void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d,
-             float scale, int left, int right, int dtype, void* stream, const int* cu = nullptr, int total = 0) {
+             float scale, int left, int right, int dtype, void* stream, const int* cu = nullptr, int total = 0,
+             const unsigned char* bmask = nullptr) {
     if (dtype == FA_BF16 && d == 256) return FA_ERR_UNSUPPORTED;
     if (B == 0 || N == 0) return FA_OK;
     if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
@@ -130,7 +138,12 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
     p.total = total;
     p.scale = scale;
     p.scale_log2 = scale * kLog2e;
-    const bool masked = window_bounds(left, right, N, p.wl, p.wr);
+    bool masked = window_bounds(left, right, N, p.wl, p.wr);
+    if (bmask != nullptr) {
+        p.bmask = bmask;
+        p.nb = (N + fa::kSparseBlock - 1) / fa::kSparseBlock;
+        masked = true;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = (dtype == FA_BF16) ? fa::launch_bwd_bf16(p, d, masked, s) : fa::launch_bwd_f32(p, d, masked, s);
     if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
@@ -272,6 +285,37 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
     if (window_left < -1 || window_right < -1) return FA_ERR_ARG;
     return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H_q, H_kv, N, d, scale,
                     window_left, window_right, dtype, stream);
+}
+
+// Checks of the block-sparse entry points beyond validate().
+static int validate_sparse(const unsigned char* bmask, int B, int N, int d, int dtype, bool& work) {
+    if (dtype != FA_BF16 || (d != 64 && d != 128) || N > FA_SPARSE_MAX_N) return FA_ERR_UNSUPPORTED;
+    work = B > 0 && N > 0;
+    if (work && !bmask) return FA_ERR_NULL;
+    return FA_OK;
+}
+
+int fa_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                       const unsigned char* block_mask, int B, int H_q, int H_kv, int N, int d, float scale,
+                       int causal, int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    bool work = false;
+    if ((st = validate_sparse(block_mask, B, N, d, dtype, work)) != FA_OK || !work) return st;
+    return fwd_impl(Q, K, V, O, LSE, B, H_q, H_kv, N, d, scale, -1, causal ? 0 : -1, dtype, stream, nullptr, 0,
+                    block_mask);
+}
+
+int fa_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                       void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                       const unsigned char* block_mask, int B, int H_q, int H_kv, int N, int d, float scale,
+                       int causal, int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    bool work = false;
+    if ((st = validate_sparse(block_mask, B, N, d, dtype, work)) != FA_OK || !work) return st;
+    return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H_q, H_kv, N, d, scale, -1,
+                    causal ? 0 : -1, dtype, stream, nullptr, 0, block_mask);
 }
 
 int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE, const int* cu_seqlens, int batch,

@@ -400,9 +400,10 @@ void bwd_dkdv3_kernel(BwdParams p) {
     // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
     // time); 2: the window (p.wl, p.wr).
     constexpr bool CAUSAL = MASK != 0;
-    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
-    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
-    const int wr_ = MASK == 2 ? p.wr : 0;
+    constexpr bool WIN = MASK >= 2;  // left bound in use (every wl_ test is guarded by it)
+    constexpr bool SPARSE = MASK == 3;  // block map p.bmask with the window
+    const int wl_ = MASK >= 2 ? p.wl : kUnbounded;
+    const int wr_ = MASK >= 2 ? p.wr : 0;
     using QL = typename Dk3Lds<D>::QL;
     constexpr int TB = Dk3Lds<D>::TILE_BYTES;
     constexpr int SB = Dk3Lds<D>::STAGE_BYTES;
@@ -456,8 +457,39 @@ void bwd_dkdv3_kernel(BwdParams p) {
     const int nqt = (N + BQ - 1) / BQ;
     const int qt_first = CAUSAL ? max(0, kstart - wr_) / BQ : 0;
     const int qt_last = WIN ? min(nqt - 1, (kstart + kDk3KeysPerWg - 1 + wl_) / BQ) : nqt - 1;
-    const int per_head = qt_last - qt_first + 1;
-    const int iters = G * per_head;  // >= 1
+    int per_head = qt_last - qt_first + 1;
+    // Block-sparse: only the query tiles whose map block (row qt * 64 / 128,
+    // column kstart / 128: one map column per workgroup) is visible, listed
+    // in LDS after the stages.
+    int* const tlist = reinterpret_cast<int*>(smem_raw + Dk3Lds<D>::BYTES);
+    if constexpr (SPARSE) {
+        const int col = kstart / kSparseBlock;
+        if (w == 0) {
+            const int cnt = compact_tiles(tlist, per_head, lane, [&](int t) {
+                return int(p.bmask[size_t((qt_first + t) * BQ / kSparseBlock) * p.nb + col] != 0);
+            });
+            if (lane == 0) tlist[kSparseListCap] = cnt;
+        }
+        __syncthreads();
+        per_head = __builtin_amdgcn_readfirstlane(lds_i32(tlist + kSparseListCap));
+    }
+    const int iters = G * per_head;  // >= 1 unless a block map hides every query tile
+    if (SPARSE && iters == 0) {
+        // no query sees these keys: their gradients are zero
+        bf16* dKh = static_cast<bf16*>(p.dK) + kvoff;
+        bf16* dVh = static_cast<bf16*>(p.dV) + kvoff;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                if (kk < N) {
+                    dKh[size_t(kk) * D + db * 32 + l32] = bf16(0.f);
+                    dVh[size_t(kk) * D + db * 32 + l32] = bf16(0.f);
+                }
+            }
+        return;
+    }
 
     int src_off[PPW];
 #pragma unroll
@@ -466,7 +498,11 @@ void bwd_dkdv3_kernel(BwdParams p) {
         QL::piece_src(w + kDkWaves * i, lane, r, e0);
         src_off[i] = r * D + e0;
     }
-    auto tile_q0 = [&](int t) { return (qt_first + t % per_head) * BQ; };
+    auto tile_q0 = [&](int t) {
+        if constexpr (SPARSE)
+            return (qt_first + (__builtin_amdgcn_readfirstlane(lds_i32(tlist + t % per_head)) & 0xFFFFFF)) * BQ;
+        else return (qt_first + t % per_head) * BQ;
+    };
     // Copy of tile t into its stage by this wave, in 2 PPW + 1 pieces: piece
     // k < PPW is a 1 KB piece of Q, k < 2 PPW of dO, and piece 2 PPW the
     // tile's LSE and D (waves 0 and 1, 16 lanes).
@@ -586,6 +622,7 @@ void bwd_dkdv3_kernel(BwdParams p) {
                     const int cc = r >> 3;
                     pb[cc] = to_bf16x8(pr[8 * cc + 0], pr[8 * cc + 1], pr[8 * cc + 2], pr[8 * cc + 3],
                                        pr[8 * cc + 4], pr[8 * cc + 5], pr[8 * cc + 6], pr[8 * cc + 7]);
+
                     sb[cc] = to_bf16x8(ds[8 * cc + 0], ds[8 * cc + 1], ds[8 * cc + 2], ds[8 * cc + 3],
                                        ds[8 * cc + 4], ds[8 * cc + 5], ds[8 * cc + 6], ds[8 * cc + 7]);
                 }
@@ -704,9 +741,10 @@ void bwd_dq2_kernel(BwdParams p) {
     // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
     // time); 2: the window (p.wl, p.wr).
     constexpr bool CAUSAL = MASK != 0;
-    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
-    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
-    const int wr_ = MASK == 2 ? p.wr : 0;
+    constexpr bool WIN = MASK >= 2;  // left bound in use (every wl_ test is guarded by it)
+    constexpr bool SPARSE = MASK == 3;  // block map p.bmask with the window
+    const int wl_ = MASK >= 2 ? p.wl : kUnbounded;
+    const int wr_ = MASK >= 2 ? p.wr : 0;
     using KL = typename DqLds<D>::KL;
     constexpr int TB = DqLds<D>::TILE_BYTES;
     constexpr int SB = DqLds<D>::STAGE_BYTES;
@@ -769,7 +807,32 @@ void bwd_dq2_kernel(BwdParams p) {
     // Key tiles [kt0, kt0 + ntiles): masked kernels see keys q - wl .. q + wr.
     const int kend = CAUSAL ? min(N, q0 + kDqBM + wr_) : N;
     const int kt0 = WIN ? max(0, q0 - wl_) / BN : 0;
-    const int ntiles = (kend + BN - 1) / BN - kt0;
+    int ntiles = (kend + BN - 1) / BN - kt0;
+    // Block-sparse: the key tiles whose map block is visible to the rows of
+    // waves 0-1 (map row q0 / 128, tag bit 0) or waves 2-3 (the next row,
+    // bit 1), listed in LDS after the stages.
+    int* const tlist = reinterpret_cast<int*>(smem_raw + DqLds<D>::BYTES);
+    if constexpr (SPARSE) {
+        const int r0 = q0 / kSparseBlock;
+        if (w == 0) {
+            const int cnt = compact_tiles(tlist, ntiles, lane, [&](int t) {
+                const int col = (kt0 + t) * BN / kSparseBlock;
+                return int(p.bmask[size_t(r0) * p.nb + col] != 0) |
+                       (r0 + 1 < p.nb && p.bmask[size_t(r0 + 1) * p.nb + col] != 0 ? 2 : 0);
+            });
+            if (lane == 0) tlist[kSparseListCap] = cnt;
+        }
+        __syncthreads();
+        ntiles = __builtin_amdgcn_readfirstlane(lds_i32(tlist + kSparseListCap));
+    }
+    auto tile_key0 = [&](int kt) -> int {
+        if constexpr (SPARSE) return (kt0 + (__builtin_amdgcn_readfirstlane(lds_i32(tlist + kt)) & 0xFFFFFF)) * BN;
+        else return (kt0 + kt) * BN;
+    };
+    auto wave_sees = [&](int kt) -> bool {
+        if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane(lds_i32(tlist + kt)) >> (24 + (w >> 1))) & 1;
+        else return true;
+    };
 
     int src_off[PPW];
 #pragma unroll
@@ -779,7 +842,7 @@ void bwd_dq2_kernel(BwdParams p) {
         src_off[i] = r * D + e0;
     }
     auto issue = [&](int kt) {
-        const int key0 = (kt0 + kt) * BN;
+        const int key0 = tile_key0(kt);
         unsigned char* st = smem_raw + (kt % NST) * SB;
         const uint32_t bytes = uint32_t(N - key0) * uint32_t(D * 2);
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kh + size_t(key0) * D, bytes);
@@ -808,11 +871,12 @@ void bwd_dq2_kernel(BwdParams p) {
         if (more) issue(kt + 2);
         const bf16* Ks = reinterpret_cast<const bf16*>(smem_raw + (kt % NST) * SB);
         const bf16* Vs = reinterpret_cast<const bf16*>(smem_raw + (kt % NST) * SB + TB);
-        const int kstart = (kt0 + kt) * BN;
+        const int kstart = tile_key0(kt);
+        const bool sees = wave_sees(kt);
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
             const int kb0 = kstart + 32 * kb;
-            if ((CAUSAL && (kb0 > wq_last + wr_ || (WIN && kb0 + 31 < wq0 - wl_))) || kb0 >= N) continue;
+            if (!sees || (CAUSAL && (kb0 > wq_last + wr_ || (WIN && kb0 + 31 < wq0 - wl_))) || kb0 >= N) continue;
             // S^T = K Q^T, dP^T = V dO^T for both row blocks: lane = query,
             // register r = key kb0 + 8(r/4) + 4hi + r%4
             f32x16 s[2], dpt[2];
@@ -902,9 +966,10 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     if (e != hipSuccess) return e;
 
     // 2. dK, dV
-    if constexpr (D == 128) {
+    constexpr size_t list_bytes = MASK == 3 ? size_t(kSparseListCap + 1) * sizeof(int) : 0;
+    if constexpr (D == 128 || MASK == 3) {
         auto kern = bwd_dkdv3_kernel<D, MASK>;
-        constexpr size_t lds = Dk3Lds<D>::BYTES;
+        constexpr size_t lds = Dk3Lds<D>::BYTES + list_bytes;
         static DeviceOnce attr;
         if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
         p.nkb = (p.N + kDk3KeysPerWg - 1) / kDk3KeysPerWg;
@@ -924,7 +989,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     // 3. dQ
     {
         auto kern = bwd_dq2_kernel<D, MASK>;
-        constexpr size_t lds = DqLds<D>::BYTES;
+        constexpr size_t lds = DqLds<D>::BYTES + list_bytes;
         static DeviceOnce attr;
         if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
         p.nqb = (p.N + kDqBM - 1) / kDqBM;
@@ -938,15 +1003,19 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd_bf16(BwdParams p, int d, int causal, hipStream_t stream) {
-    // 0: no mask, 1: causal, 2: a general window
-    const int mk = !causal ? 0 : (p.wl >= kUnbounded && p.wr == 0) ? 1 : 2;
+    // 0: no mask, 1: causal, 2: a general window, 3: block map (and window)
+    const int mk = p.bmask != nullptr ? 3 : !causal ? 0 : (p.wl >= kUnbounded && p.wr == 0) ? 1 : 2;
     switch (d) {
         case 64:
-            return mk == 0 ? launch_bwd_t<64, 0>(p, stream)
-                           : mk == 1 ? launch_bwd_t<64, 1>(p, stream) : launch_bwd_t<64, 2>(p, stream);
+            return mk == 0   ? launch_bwd_t<64, 0>(p, stream)
+                   : mk == 1 ? launch_bwd_t<64, 1>(p, stream)
+                   : mk == 2 ? launch_bwd_t<64, 2>(p, stream)
+                             : launch_bwd_t<64, 3>(p, stream);
         case 128:
-            return mk == 0 ? launch_bwd_t<128, 0>(p, stream)
-                           : mk == 1 ? launch_bwd_t<128, 1>(p, stream) : launch_bwd_t<128, 2>(p, stream);
+            return mk == 0   ? launch_bwd_t<128, 0>(p, stream)
+                   : mk == 1 ? launch_bwd_t<128, 1>(p, stream)
+                   : mk == 2 ? launch_bwd_t<128, 2>(p, stream)
+                             : launch_bwd_t<128, 3>(p, stream);
         default: return hipErrorNotSupported;
     }
 }

@@ -99,6 +99,27 @@ __device__ __forceinline__ f32x4 lds_f32x4(const float* __restrict__ p) {
     return *reinterpret_cast<const f32x4*>(p);
 }
 
+__device__ __forceinline__ int lds_i32(const int* __restrict__ p) { return *p; }
+
+// Compacts, within one wave, the indices t in [0, n) whose tag(t) is
+// nonzero into list[0 .. count) in ascending order, each stored as
+// t | tag(t) << 24 (t < 2^24, tag < 128); returns count (wave-uniform).
+template <typename F>
+__device__ __forceinline__ int compact_tiles(int* list, int n, int lane, F tag) {
+    int count = 0;
+    for (int base = 0; base < n; base += 64) {
+        const int t = base + lane;
+        const int tg = t < n ? tag(t) : 0;
+        const unsigned long long bal = __ballot(tg != 0);
+        if (tg != 0) {
+            const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(bal >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0));
+            list[count + below] = t | (tg << 24);
+        }
+        count += __popcll(bal);
+    }
+    return count;
+}
+
 // Transposing 8-byte LDS read (see the layout note at the top).
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* __restrict__ p) {
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;

@@ -391,11 +391,13 @@ template <int D, int MASK>
 __global__ __launch_bounds__(kPPWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(FwdParams p) {
     // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
-    // time); 2: the window (p.wl, p.wr).
+    // time); 2: the window (p.wl, p.wr); 3: the block map p.bmask together
+    // with the window (p.wl, p.wr).
     constexpr bool CAUSAL = MASK != 0;
-    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
-    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
-    const int wr_ = MASK == 2 ? p.wr : 0;
+    constexpr bool WIN = MASK >= 2;  // left bound in use (every wl_ test is guarded by it)
+    constexpr bool SPARSE = MASK == 3;
+    const int wl_ = MASK >= 2 ? p.wl : kUnbounded;
+    const int wr_ = MASK >= 2 ? p.wr : 0;
     constexpr int BN = kPPBN;
     constexpr int NST = kPPStages;
     constexpr int BM = kPPBM;
@@ -435,7 +437,33 @@ void fwd_pp_kernel(FwdParams p) {
     // q - wl .. q + wr of each query q (causal: wl unbounded, wr = 0).
     const int kend = CAUSAL ? min(N, q0 + BM + wr_) : N;
     const int kt0 = WIN ? max(0, q0 - wl_) / BN : 0;
-    const int T = (kend + BN - 1) / BN - kt0;
+    int T = (kend + BN - 1) / BN - kt0;
+    // Block-sparse: the tiles of that range whose map block is visible to
+    // group A (map row q0 / 128, tag bit 0) or group B (the next row, bit 1),
+    // listed in LDS after the stages; j below then indexes the list.
+    int* const tlist = reinterpret_cast<int*>(smem_raw + pp_lds_bytes<D>());
+    if constexpr (SPARSE) {
+        const int r0 = q0 / kSparseBlock;
+        if (w == 0) {
+            const int cnt = compact_tiles(tlist, T, lane, [&](int t) {
+                const int col = (kt0 + t) * BN / kSparseBlock;
+                return int(p.bmask[size_t(r0) * p.nb + col] != 0) |
+                       (r0 + 1 < p.nb && p.bmask[size_t(r0 + 1) * p.nb + col] != 0 ? 2 : 0);
+            });
+            if (lane == 0) tlist[kSparseListCap] = cnt;
+        }
+        __syncthreads();
+        T = __builtin_amdgcn_readfirstlane(lds_i32(tlist + kSparseListCap));
+    }
+    // First key of tile j, and (block-sparse) which groups see it.
+    auto tile_key0 = [&](int j) -> int {
+        if constexpr (SPARSE) return (kt0 + (__builtin_amdgcn_readfirstlane(lds_i32(tlist + j)) & 0xFFFFFF)) * BN;
+        else return (kt0 + j) * BN;
+    };
+    auto group_sees = [&](int j) -> bool {
+        if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane(lds_i32(tlist + j)) >> (24 + grp)) & 1;
+        else return true;
+    };
 
     // Q rows first (the oldest loads of the wave), then the prologue tiles
     // 0 .. min(T, NST) - 1 into the empty stages.
@@ -451,7 +479,7 @@ void fwd_pp_kernel(FwdParams p) {
     cp.init(w, lane);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
-        if (t < T) cp.issue(Kh, Vh, smem + t * 2 * TILE, smem + t * 2 * TILE + TILE, (kt0 + t) * BN, N);
+        if (t < T) cp.issue(Kh, Vh, smem + t * 2 * TILE, smem + t * 2 * TILE + TILE, tile_key0(t), N);
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -475,7 +503,8 @@ void fwd_pp_kernel(FwdParams p) {
     // Number of 32-key blocks of tile j this wave must process (uniform).
     auto active_kb = [&](int j) -> int {
         if (!CAUSAL) return KB;
-        const int kstart = (kt0 + j) * BN;
+        if (!group_sees(j)) return 0;
+        const int kstart = tile_key0(j);
         if (kstart > wq_last + wr_ || (WIN && kstart + BN - 1 < wq0 - wl_)) return 0;
         return min(KB, (wq_last + wr_ - kstart) / 32 + 1);
     };
@@ -495,7 +524,7 @@ void fwd_pp_kernel(FwdParams p) {
             const int t = step / 2 + 2;
             if (t < T) {
                 bf16* st = smem + (t % NST) * 2 * TILE;
-                cp.issue(Kh, Vh, st, st + TILE, (kt0 + t) * BN, N);
+                cp.issue(Kh, Vh, st, st + TILE, tile_key0(t), N);
             }
         }
     };
@@ -576,7 +605,7 @@ void fwd_pp_kernel(FwdParams p) {
     // ---- V phase j: online softmax of S_j -> P_j (bf16), O rescaled if needed.
     auto phase_v = [&](int j) {
         if (j >= T || active_kb(j) == 0) return;
-        const int kstart = (kt0 + j) * BN;
+        const int kstart = tile_key0(j);
         const bool mask_hi = (CAUSAL && kstart + BN - 1 > wq0 + wr_) || (kstart + BN > N);
         const bool mask_lo = WIN && kstart < wq_last - wl_;
         if (mask_hi && !mask_lo) {
@@ -650,7 +679,9 @@ void fwd_pp_kernel(FwdParams p) {
     }
 
     const float lt = half_swap_sum(l);
-    const float inv = 1.f / lt;
+    // A row that sees no key at all (block-sparse only) has l = 0: O = 0,
+    // LSE = -inf.
+    const float inv = (!SPARSE || lt > 0.f) ? 1.f / lt : 0.f;
     if (qrow < N) {
         bf16* orow = Oh + size_t(qrow) * D;
 #pragma unroll
@@ -662,14 +693,15 @@ void fwd_pp_kernel(FwdParams p) {
                 *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * jj + 4 * hi) = v;
             }
         }
-        if (hi == 0 && p.LSE != nullptr) p.LSE[sq.qrow(h) + qrow] = (m + fast_log2(lt)) * kLn2;
+        if (hi == 0 && p.LSE != nullptr)
+            p.LSE[sq.qrow(h) + qrow] = (!SPARSE || lt > 0.f) ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
     }
 }
 
 template <int D, int MASK>
 hipError_t launch_fwd_pp_t(FwdParams p, hipStream_t stream) {
     auto kern = fwd_pp_kernel<D, MASK>;
-    constexpr size_t lds = pp_lds_bytes<D>();
+    constexpr size_t lds = pp_lds_bytes<D>() + (MASK == 3 ? size_t(kSparseListCap + 1) * sizeof(int) : 0);
     static DeviceOnce attr;
     const hipError_t e = set_max_dynamic_lds(kern, lds, attr);
     if (e != hipSuccess) return e;
@@ -706,8 +738,14 @@ hipError_t launch_fwd_bf16(FwdParams p, int d, int causal, hipStream_t stream) {
         p.qmode = 2;
         p.scale_log2 = 1.f;
     }
-    // 0: no mask, 1: causal, 2: a general window
-    const int mk = !causal ? 0 : (p.wl >= kUnbounded && p.wr == 0) ? 1 : 2;
+    // 0: no mask, 1: causal, 2: a general window, 3: block map (and window)
+    const int mk = p.bmask != nullptr ? 3 : !causal ? 0 : (p.wl >= kUnbounded && p.wr == 0) ? 1 : 2;
+    if (mk == 3) {
+        // d = 64 / 128 only (the entry point checks)
+        if (d == 64) return launch_fwd_pp_t<64, 3>(p, stream);
+        if (d == 128) return launch_fwd_pp_t<128, 3>(p, stream);
+        return hipErrorNotSupported;
+    }
 #define FA_FWD_DISPATCH(L, DD) \
     (mk == 0 ? L<DD, 0>(p, stream) : mk == 1 ? L<DD, 1>(p, stream) : L<DD, 2>(p, stream))
     switch (d) {

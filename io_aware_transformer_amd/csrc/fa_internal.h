@@ -32,9 +32,20 @@ struct FwdParams {
     // the longest sequence (the grid's row bound).
     const int* cu;
     int total;
+    // Block-sparse map (MASK 3 kernels): nb x nb bytes in device memory,
+    // nb = ceil(N / kSparseBlock); query i sees key j only when
+    // bmask[(i / kSparseBlock) * nb + j / kSparseBlock] != 0 (and the window
+    // (wl, wr) allows it).
+    const unsigned char* bmask;
+    int nb;
 };
 
 constexpr int kUnbounded = 1 << 30;
+// Block-sparse attention: positions per map block, and the longest sequence
+// the kernels' per-workgroup tile lists (64-row / 64-key tiles, in LDS) hold.
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxN = 1 << 16;
+constexpr int kSparseListCap = kSparseMaxN / 64;
 
 // Backward launch parameters.
 struct BwdParams {
@@ -55,6 +66,8 @@ struct BwdParams {
     int wl, wr;        // window of the masked kernels, as FwdParams
     const int* cu;     // packed sequences, as FwdParams (Drow is then [Hq, total])
     int total;
+    const unsigned char* bmask;  // block-sparse map, as FwdParams
+    int nb;
 };
 
 // Split key/value forward parameters.  Q [B, Hq, Nq, d], K/V [B, Hkv, Nk, d]

@@ -69,3 +69,19 @@ def test_good_buffers_reach_the_device_check(i):
         call(torch.zeros(oshape, dtype=dt), torch.zeros(lshape, dtype=torch.float32))
     with pytest.raises(ValueError, match="HIP device"):
         call(None, None)
+
+
+def test_block_mask_validated_before_the_device_check():
+    from io_aware_transformer_amd import bwd_blocksparse, fwd_blocksparse
+
+    q, k, v = _qkv(N=300)
+    good = torch.ones((3, 3), dtype=torch.uint8)
+    for bad in (torch.ones((2, 2), dtype=torch.uint8), torch.ones((3, 3), dtype=torch.int32),
+                torch.ones((3, 6), dtype=torch.uint8)[:, ::2]):
+        with pytest.raises(ValueError, match="block_mask"):
+            fwd_blocksparse(q, k, v, bad)
+    with pytest.raises(ValueError, match="HIP device"):
+        fwd_blocksparse(q, k, v, good)
+    lse = torch.zeros((1, 2, 300))
+    with pytest.raises(ValueError, match="block_mask"):
+        bwd_blocksparse(q, k, v, q, lse, q, torch.ones((4, 4), dtype=torch.uint8))
