@@ -12,11 +12,13 @@ backward, in float64, one (batch, query-head) unit at a time, plus
 attention with queries and keys of different lengths, attention over a key
 range, the merge of partial results over disjoint key ranges, local
 (sliding-window) attention, batches of packed sequences of different
-lengths and block-sparse attention.  Every function cites the passage of the source pages it follows;
+lengths, block-sparse attention and attention with dropout on the
+probabilities (keep mask from Philox-4x32-10).  Every function cites the passage of the source pages it follows;
 see ``oracle/attention.py``, ``oracle/splitkv.py``, ``oracle/window.py`` and
-``oracle/varlen.py`` and ``oracle/blocksparse.py``.
+``oracle/varlen.py``, ``oracle/blocksparse.py`` and ``oracle/dropout.py``.
 """
 
+from .dropout import dropout_backward, dropout_forward, dropout_threshold, keep_mask, philox4x32_10
 from .blocksparse import blocksparse_backward, blocksparse_forward, blocksparse_visible
 from .attention import (
     attention_forward,
@@ -48,4 +50,9 @@ __all__ = [
     "blocksparse_forward",
     "blocksparse_backward",
     "blocksparse_visible",
+    "dropout_forward",
+    "dropout_backward",
+    "dropout_threshold",
+    "keep_mask",
+    "philox4x32_10",
 ]

@@ -18,6 +18,7 @@ import numpy as np
 
 import oracle.attention as OA
 import oracle.blocksparse as OB
+import oracle.dropout as ODR
 import oracle.splitkv as OS
 import oracle.varlen as OV
 import oracle.window as OW
@@ -695,6 +696,121 @@ def check_blocksparse_finite_differences(seed=45):
                 assert abs(fd - G[ix]) < 1e-7 * max(1.0, abs(fd)), (ix, fd, G[ix])
 
 
+# ---------------------------------------------------------------- dropout (Philox-4x32-10)
+
+
+def check_philox_known_answers():
+    """The generator reproduces the published known-answer values
+    (tests/golden/philox4x32_10_kat.txt)."""
+    rows = []
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append([int(x, 16) for x in line.split()])
+    assert len(rows) == 3
+    for r in rows:
+        got = ODR.philox4x32_10(*r[:4], *r[4:6])
+        assert [int(x) for x in got] == r[6:], (r, [hex(int(x)) for x in got])
+
+
+def check_dropout_mask_layout(seed=51):
+    """Element (i, j) of unit bh is byte j % 4 of word i % 4 of the Philox
+    block with counter (j // 4, i // 4, bh, offset): the vectorised mask
+    equals that lookup done one element at a time; the keep rule is u >= t8."""
+    rng = np.random.default_rng(seed)
+    n, bh, sd, off, p = 37, 5, 0x1234567890ABCDEF, 3, 0.3
+    keep = ODR.keep_mask(n, n, bh, p, sd, off)
+    t8 = ODR.dropout_threshold(p)
+    assert t8 == 77
+    for _ in range(60):
+        i, j = int(rng.integers(n)), int(rng.integers(n))
+        w = ODR.philox4x32_10(j // 4, i // 4, bh, off, sd & 0xFFFFFFFF, sd >> 32)[i % 4]
+        u = (int(w) >> (8 * (j % 4))) & 0xFF
+        assert keep[i, j] == (u >= t8), (i, j)
+    # different units, offsets and seeds give different masks
+    assert not np.array_equal(keep, ODR.keep_mask(n, n, bh + 1, p, sd, off))
+    assert not np.array_equal(keep, ODR.keep_mask(n, n, bh, p, sd, off + 1))
+    assert not np.array_equal(keep, ODR.keep_mask(n, n, bh, p, sd + 1, off))
+
+
+def check_dropout_keep_rate(seed=52):
+    """Bytes are uniform: the kept fraction is 1 - t8 / 256 to within five
+    standard deviations, and every byte value occurs about equally often."""
+    n = 512
+    for p in (0.1, 0.5, 0.75):
+        keep = ODR.keep_mask(n, n, 2, p, 0xDEADBEEF + seed, 0)
+        q = 1.0 - ODR.dropout_threshold(p) / 256.0
+        sd = math.sqrt(q * (1 - q) / keep.size)
+        assert abs(keep.mean() - q) < 5 * sd, (p, keep.mean(), q)
+    i = np.arange(256)[:, None]
+    j = np.arange(256)[None, :]
+    words = ODR.philox4x32_10(j // 4, i // 4, 0, 0, 7, 9)
+    u = (np.choose(i % 4, words) >> (8 * (j % 4)).astype(np.uint32)) & np.uint32(0xFF)
+    counts = np.bincount(u.ravel(), minlength=256)
+    expect = u.size / 256
+    chi2 = float(((counts - expect) ** 2 / expect).sum())
+    assert chi2 < 400, chi2  # 255 degrees of freedom
+
+
+def check_dropout_zero_probability(seed=53):
+    """p = 0 keeps everything: plain attention, forward and backward."""
+    rng = np.random.default_rng(seed)
+    Q, K, V = _qkv(rng, 2, 4, 2, 13, 13, 6)
+    dO = rng.standard_normal(Q.shape)
+    for causal in (False, True):
+        O, L = ODR.dropout_forward(Q, K, V, 0.4, causal, 0.0, 99)
+        Or, Lr = OA.attention_forward(Q, K, V, 0.4, causal)
+        assert np.max(np.abs(O - Or)) < 1e-14 and np.max(np.abs(L - Lr)) < 1e-13
+        g = ODR.dropout_backward(Q, K, V, dO, 0.4, causal, 0.0, 99)
+        gr = OA.attention_backward(Q, K, V, dO, 0.4, causal)
+        for a, b in zip(g, gr):
+            assert np.max(np.abs(a - b)) < 1e-13
+
+
+def check_dropout_unbiased(seed=54):
+    """Inverted dropout keeps the expectation: O averaged over many seeds
+    approaches plain attention (standard error about 0.005 here), and the
+    LSE never changes."""
+    rng = np.random.default_rng(seed)
+    Q, K, V = _qkv(rng, 1, 1, 1, 12, 12, 3)
+    Or, Lr = OA.attention_forward(Q, K, V, 0.5, False)
+    acc = np.zeros_like(Or)
+    S = 3000
+    for s in range(S):
+        O, L = ODR.dropout_forward(Q, K, V, 0.5, False, 0.25, s, 0)
+        acc += O
+        if s < 3:
+            assert np.max(np.abs(L - Lr)) < 1e-13
+    assert np.max(np.abs(acc / S - Or)) < 0.05
+    # one seed: O is visibly different from plain attention
+    O1, _ = ODR.dropout_forward(Q, K, V, 0.5, False, 0.25, 1, 0)
+    assert np.max(np.abs(O1 - Or)) > 0.05
+
+
+def check_dropout_finite_differences(seed=55):
+    """Central differences of <dO, O> with the mask fixed by (seed, offset),
+    grouped heads, causal and not."""
+    rng = np.random.default_rng(seed)
+    Q, K, V = _qkv(rng, 1, 2, 1, 9, 9, 3)
+    dO = rng.standard_normal(Q.shape)
+    sc, h, p, sd = 0.7, 1e-6, 0.3, 12345
+    for causal in (False, True):
+        dQ, dK, dV = ODR.dropout_backward(Q, K, V, dO, sc, causal, p, sd, 2)
+
+        def loss(q, k, v):
+            return float((ODR.dropout_forward(q, k, v, sc, causal, p, sd, 2)[0] * dO).sum())
+
+        for X, G in ((Q, dQ), (K, dK), (V, dV)):
+            for _ in range(6):
+                ix = tuple(int(rng.integers(0, s)) for s in X.shape)
+                Xp, Xm = X.copy(), X.copy()
+                Xp[ix] += h
+                Xm[ix] -= h
+                fd = (loss(*[Xp if Y is X else Y for Y in (Q, K, V)]) -
+                      loss(*[Xm if Y is X else Y for Y in (Q, K, V)])) / (2 * h)
+                assert abs(fd - G[ix]) < 1e-7 * max(1.0, abs(fd)), (ix, fd, G[ix])
+
+
 ALL_CHECKS = [
     check_four_token_tiles_consistent,
     check_four_token_recurrence_values,
@@ -725,4 +841,10 @@ ALL_CHECKS = [
     check_blocksparse_rows_are_gathers,
     check_blocksparse_empty_rows,
     check_blocksparse_finite_differences,
+    check_philox_known_answers,
+    check_dropout_mask_layout,
+    check_dropout_keep_rate,
+    check_dropout_zero_probability,
+    check_dropout_unbiased,
+    check_dropout_finite_differences,
 ]

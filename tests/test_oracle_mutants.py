@@ -9,6 +9,7 @@ import pytest
 
 import oracle.attention as OA
 import oracle.blocksparse as OB
+import oracle.dropout as ODR
 import oracle.splitkv as OS
 import oracle.varlen as OV
 import oracle.window as OW
@@ -271,6 +272,66 @@ def _bs_bwd_no_rowterm(Q, K, V, dO, mask, scale, causal):
 OB_orig = {"blocksparse_visible": OB.blocksparse_visible, "_probs": OB._probs}
 
 
+def _philox_words_swapped(c0, c1, c2, c3, k0, k1):
+    w = ODR_orig["philox4x32_10"](c0, c1, c2, c3, k0, k1)
+    return [w[1], w[0], w[3], w[2]]
+
+
+def _philox_no_key_bump(c0, c1, c2, c3, k0, k1):
+    c = [np.asarray(x, dtype=np.uint64) & np.uint64(0xFFFFFFFF) for x in (c0, c1, c2, c3)]
+    c = list(np.broadcast_arrays(*c))
+    for _ in range(10):
+        p0 = np.uint64(0xD2511F53) * c[0]
+        p1 = np.uint64(0xCD9E8D57) * c[2]
+        c = [(p1 >> np.uint64(32)) ^ c[1] ^ np.uint64(k0), p1 & np.uint64(0xFFFFFFFF),
+             (p0 >> np.uint64(32)) ^ c[3] ^ np.uint64(k1), p0 & np.uint64(0xFFFFFFFF)]
+    return [x.astype(np.uint32) for x in c]
+
+
+def _keep_counter_swapped(n_q, n_k, bh, p, seed, offset):
+    t8 = ODR.dropout_threshold(p)
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    words = ODR.philox4x32_10(i // 4, j // 4, bh, offset, seed & 0xFFFFFFFF, seed >> 32)
+    u = (np.choose(i % 4, words) >> (8 * (j % 4)).astype(np.uint32)) & np.uint32(0xFF)
+    return u >= t8
+
+
+def _keep_byte_by_query(n_q, n_k, bh, p, seed, offset):
+    t8 = ODR.dropout_threshold(p)
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    words = ODR.philox4x32_10(j // 4, i // 4, bh, offset, seed & 0xFFFFFFFF, seed >> 32)
+    u = (np.choose(j % 4, words) >> (8 * (i % 4)).astype(np.uint32)) & np.uint32(0xFF)
+    return u >= t8
+
+
+def _dropout_unit_unscaled(q, k, scale, causal, keep, t8):
+    p, m, l = OA._row_softmax(OA._scores(q, k, scale, causal))
+    return p, np.where(keep, p, 0.0), m + np.log(l)
+
+
+def _dropout_bwd_dp_unmasked(Q, K, V, dO, scale, causal, p, seed, offset=0):
+    Q, K, V, dO = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, dO))
+    B, Hq, Hkv, N, d = OA._check_shapes(Q, K, V)
+    t8 = ODR.dropout_threshold(p)
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = OA.kv_head_of(h, Hq, Hkv)
+            keep = ODR.keep_mask(N, N, b * Hq + h, p, seed, offset)
+            pr, pz, _ = ODR._unit(Q[b, h], K[b, g], scale, causal, keep, t8)
+            dp = dO[b, h] @ V[b, g].T
+            ds = pr * (dp - (pr * dp).sum(axis=1)[:, None])
+            dQ[b, h] = scale * (ds @ K[b, g])
+            dK[b, g] += scale * (ds.T @ Q[b, h])
+            dV[b, g] += pz.T @ dO[b, h]
+    return dQ, dK, dV
+
+
+ODR_orig = {"philox4x32_10": ODR.philox4x32_10}
+
+
 MUTANTS = {
     "scale_dropped": ("_scores", _scores_no_scale),
     "scale_twice": ("_scores", _scores_scale_twice),
@@ -304,6 +365,12 @@ MUTANTS = {
     "blocksparse_blocks_of_64": (OB, "blocksparse_visible", _bs_visible_block64),
     "blocksparse_empty_rows_see_all": (OB, "_probs", _bs_probs_empty_rows_see_all),
     "blocksparse_bwd_missing_row_term": (OB, "blocksparse_backward", _bs_bwd_no_rowterm),
+    "philox_output_words_swapped": (ODR, "philox4x32_10", _philox_words_swapped),
+    "philox_key_not_bumped": (ODR, "philox4x32_10", _philox_no_key_bump),
+    "dropout_counter_query_key_swapped": (ODR, "keep_mask", _keep_counter_swapped),
+    "dropout_byte_chosen_by_query": (ODR, "keep_mask", _keep_byte_by_query),
+    "dropout_not_rescaled": (ODR, "_unit", _dropout_unit_unscaled),
+    "dropout_bwd_dp_unmasked": (ODR, "dropout_backward", _dropout_bwd_dp_unmasked),
 }
 
 
