@@ -217,6 +217,43 @@ int fa_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* 
                        int dtype, void* stream);
 
 /*
+ * Dropout on the attention probabilities.  The deep-dive page ("Flash
+ * attention: fast and memory-efficient exact attention with IO-awareness --
+ * a deep dive", "Computing and memory basics", quantitative evidence) names
+ * dropout with softmax and masking as the steps that dominate unfused
+ * attention; it gives no formula or generator.  Reading (inverted dropout on
+ * P, with a counter-based generator so that the backward regenerates the
+ * forward's mask instead of storing it):
+ *   O = (P o Z) V / (1 - p8),   LSE as without dropout,
+ *   dV = (P o Z)^T dO / (1 - p8),  dP = (dO V^T) o Z / (1 - p8),
+ *   dS = P o (dP - D) with D_i = dO_i . O_i,  dQ, dK as fa_bwd.
+ * The mask: t8 = round(dropout_p * 256) (half to even), p8 = t8 / 256; the
+ * 4 x 4 block of queries 4a..4a+3 and keys 4c..4c+3 of batch b and query
+ * head h takes the four 32-bit words of Philox-4x32-10 (J. K. Salmon et al.,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011) with
+ *   key (seed & 0xFFFFFFFF, seed >> 32), counter (c, a, b * H_q + h, offset);
+ * word i % 4 belongs to query i, its byte j % 4 (bits 8 (j % 4) .. +7) to key
+ * j, and Z_ij = 1 when that byte >= t8.
+ *
+ * fa_fwd_dropout / fa_bwd_dropout -- as fa_fwd / fa_bwd plus dropout_p
+ * (0 <= dropout_p, rounding to t8 <= 255, else FA_ERR_ARG; t8 = 0 is plain
+ * attention), seed and offset.  fa_bwd_dropout must get O and LSE of
+ * fa_fwd_dropout with the same dropout_p, seed, offset, scale and causal
+ * flag.  FA_BF16 with d in {64, 128}; other valid combinations return
+ * FA_ERR_UNSUPPORTED.
+ */
+int fa_fwd_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int H_q, int H_kv, int N, int d, float scale, int causal,
+                   float dropout_p, unsigned long long seed, unsigned int offset,
+                   int dtype, void* stream);
+int fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int H_q, int H_kv, int N, int d, float scale, int causal,
+                   float dropout_p, unsigned long long seed, unsigned int offset,
+                   int dtype, void* stream);
+
+/*
  * Packed variable-length batches.  The interview Q&A page (app.wittybyte.ai,
  * "FlashAttention1", scaling-challenges answer) names uneven work across the
  * GPU's cores for variable sequence lengths and gives no layout.  Reading:

@@ -54,6 +54,8 @@ EXPORTS = (
     "fa_bwd_noalloc",
     "fa_fwd_blocksparse",
     "fa_bwd_blocksparse",
+    "fa_fwd_dropout",
+    "fa_bwd_dropout",
 )
 
 
@@ -128,6 +130,13 @@ def load():
     # Q K V O dO LSE dQ dK dV workspace | bytes | mask | B H_q H_kv N d | scale | causal dtype | stream
     lib.fa_bwd_blocksparse.argtypes = [_vp] * 10 + [ctypes.c_size_t, _vp] + [_i] * 5 + [_f, _i, _i, _vp]
     lib.fa_bwd_blocksparse.restype = _i
+    _u64, _u32 = ctypes.c_ulonglong, ctypes.c_uint
+    # Q K V O LSE | B H_q H_kv N d | scale | causal | p seed offset | dtype stream
+    lib.fa_fwd_dropout.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _f, _u64, _u32, _i, _vp]
+    lib.fa_fwd_dropout.restype = _i
+    # Q K V O dO LSE dQ dK dV workspace | bytes | B H_q H_kv N d | scale | causal | p seed offset | dtype stream
+    lib.fa_bwd_dropout.argtypes = [_vp] * 10 + [ctypes.c_size_t] + [_i] * 5 + [_f, _i, _f, _u64, _u32, _i, _vp]
+    lib.fa_bwd_dropout.restype = _i
     _lib = lib
     return lib
 

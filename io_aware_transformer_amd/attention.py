@@ -344,3 +344,47 @@ def bwd_blocksparse(q, k, v, o, lse, do, block_mask, scale=None, causal=False, w
     )
     _lib.check(st, "fa_bwd_blocksparse")
     return dq, dk, dv
+
+
+def fwd_dropout(q, k, v, dropout_p, seed, offset=0, scale=None, causal=True, out=None, lse=None):
+    """Forward with dropout on the attention probabilities (inverted: kept
+    terms scaled by 256 / (256 - t8), t8 = round(dropout_p * 256)); the keep
+    mask is a function of (seed, offset, batch, head, query, key).  LSE is
+    that of the softmax without dropout.  Returns (o, lse) as ``fwd``."""
+    B, Hq, Hkv, N, d = _check(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = _buffer(out, q.shape, q.dtype, q.device, "out")
+    lse = _buffer(lse, (B, Hq, N), torch.float32, q.device, "lse")
+    _on_device(q)
+    st = _lib.load().fa_fwd_dropout(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        lse.data_ptr() or None, B, Hq, Hkv, N, d, float(scale), int(bool(causal)), float(dropout_p),
+        int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 32 - 1), _DTYPES[q.dtype], _stream(q.device),
+    )
+    _lib.check(st, "fa_fwd_dropout")
+    return o, lse
+
+
+def bwd_dropout(q, k, v, o, lse, do, dropout_p, seed, offset=0, scale=None, causal=True, workspace=None):
+    """Backward of ``fwd_dropout`` with the same dropout_p, seed and offset:
+    returns (dq, dk, dv)."""
+    B, Hq, Hkv, N, d = _check(q, k, v, o, do)
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H_q, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    _on_device(q)
+    st = _lib.load().fa_bwd_dropout(
+        q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+        do.data_ptr() or None, lse.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,
+        dv.data_ptr() or None, workspace.data_ptr() or None, workspace.numel(), B, Hq, Hkv, N, d, float(scale),
+        int(bool(causal)), float(dropout_p), int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 32 - 1),
+        _DTYPES[q.dtype], _stream(q.device),
+    )
+    _lib.check(st, "fa_bwd_dropout")
+    return dq, dk, dv

@@ -73,9 +73,16 @@ bool window_bounds(int left, int right, int N, int& wl, int& wr) {
 
 // Fixed-length batches pass cu == nullptr; packed sequences pass the device
 // offsets, the packed row count `total` and the longest length as N.
+// Dropout of the dropout entry points (t8 = 0: none).
+struct Drop {
+    int t8 = 0;
+    unsigned long long seed = 0;
+    unsigned int offset = 0;
+};
+
 int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N, int d,
              float scale, int left, int right, int dtype, void* stream, const int* cu = nullptr, int total = 0,
-             const unsigned char* bmask = nullptr) {
+             const unsigned char* bmask = nullptr, Drop drop = Drop()) {
     if (B == 0 || N == 0) return FA_OK;
     if (!Q || !K || !V || !O) return FA_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 16))
@@ -99,6 +106,10 @@ int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, i
         p.nb = (N + fa::kSparseBlock - 1) / fa::kSparseBlock;
         masked = true;
     }
+    p.drop_t8 = drop.t8;
+    p.drop_k0 = uint32_t(drop.seed & 0xFFFFFFFFull);
+    p.drop_k1 = uint32_t(drop.seed >> 32);
+    p.drop_off = drop.offset;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = (dtype == FA_BF16) ? fa::launch_fwd_bf16(p, d, masked, s) : fa::launch_fwd_f32(p, d, masked, s);
     if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
@@ -109,7 +120,7 @@ int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, i
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
              void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d,
              float scale, int left, int right, int dtype, void* stream, const int* cu = nullptr, int total = 0,
-             const unsigned char* bmask = nullptr) {
+             const unsigned char* bmask = nullptr, Drop drop = Drop()) {
     if (dtype == FA_BF16 && d == 256) return FA_ERR_UNSUPPORTED;
     if (B == 0 || N == 0) return FA_OK;
     if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
@@ -144,6 +155,10 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
         p.nb = (N + fa::kSparseBlock - 1) / fa::kSparseBlock;
         masked = true;
     }
+    p.drop_t8 = drop.t8;
+    p.drop_k0 = uint32_t(drop.seed & 0xFFFFFFFFull);
+    p.drop_k1 = uint32_t(drop.seed >> 32);
+    p.drop_off = drop.offset;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = (dtype == FA_BF16) ? fa::launch_bwd_bf16(p, d, masked, s) : fa::launch_bwd_f32(p, d, masked, s);
     if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
@@ -316,6 +331,45 @@ int fa_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* 
     if ((st = validate_sparse(block_mask, B, N, d, dtype, work)) != FA_OK || !work) return st;
     return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H_q, H_kv, N, d, scale, -1,
                     causal ? 0 : -1, dtype, stream, nullptr, 0, block_mask);
+}
+
+// Dropout probability -> 8-bit threshold t8 = round(p * 256) (half to
+// even); FA_ERR_ARG unless 0 <= t8 <= 255.
+static int dropout_t8(float p, int& t8) {
+    if (!std::isfinite(p) || p < 0.f) return FA_ERR_ARG;
+    const double x = std::nearbyint(double(p) * 256.0);
+    if (x > 255.0) return FA_ERR_ARG;
+    t8 = int(x);
+    return FA_OK;
+}
+
+int fa_fwd_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int N,
+                   int d, float scale, int causal, float dropout_p, unsigned long long seed, unsigned int offset,
+                   int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    Drop dr;
+    if ((st = dropout_t8(dropout_p, dr.t8)) != FA_OK) return st;
+    if (dtype != FA_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    dr.seed = seed;
+    dr.offset = offset;
+    return fwd_impl(Q, K, V, O, LSE, B, H_q, H_kv, N, d, scale, causal ? -1 : -2, causal ? 0 : -2, dtype, stream,
+                    nullptr, 0, nullptr, dr);
+}
+
+int fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                   void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv,
+                   int N, int d, float scale, int causal, float dropout_p, unsigned long long seed, unsigned int offset,
+                   int dtype, void* stream) {
+    int st = validate(B, H_q, H_kv, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    Drop dr;
+    if ((st = dropout_t8(dropout_p, dr.t8)) != FA_OK) return st;
+    if (dtype != FA_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    dr.seed = seed;
+    dr.offset = offset;
+    return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H_q, H_kv, N, d, scale,
+                    causal ? -1 : -2, causal ? 0 : -2, dtype, stream, nullptr, 0, nullptr, dr);
 }
 
 int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE, const int* cu_seqlens, int batch,

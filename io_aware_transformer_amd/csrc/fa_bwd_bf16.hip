@@ -127,7 +127,7 @@ constexpr int dk_keys_per_wg() {
     return 32 * DkCfg<D>::KPW * kDkWaves;
 }
 
-template <int D, int MASK>
+template <int D, int MASK, bool DROP>
 __global__ __launch_bounds__(kDkWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv2_kernel(BwdParams p) {
     // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
@@ -294,12 +294,29 @@ void bwd_dkdv2_kernel(BwdParams p) {
 #pragma unroll
             for (int kb = 0; kb < KPW; ++kb) {
                 float pr[16], ds[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    pr[r] = fast_exp2(fmaf(sacc[kb][r], c, -lq[r]));
-                    ds[r] = pr[r] * (dpacc[kb][r] - dq[r]);
-                }
                 const int key0 = kw0 + 32 * kb;
+                if constexpr (DROP) {
+                    // Dropout: P enters dV dropped (its 256 / (256 - t8)
+                    // factor is applied to dV at the end); dP = dO V^T is
+                    // dropped and scaled before dS.
+                    uint32_t dy[4];
+                    drop_bytes_kmajor(dy, key0 + l32, qb0, hi, lane, uint32_t(b * p.Hq + g * G + t / per_head),
+                                      p.drop_off, p.drop_k0, p.drop_k1);
+                    const float dinv = 256.f / float(256 - p.drop_t8);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const bool kp = drop_keep(dy, r, p.drop_t8);
+                        pr[r] = fast_exp2(fmaf(sacc[kb][r], c, -lq[r]));
+                        ds[r] = pr[r] * ((kp ? dpacc[kb][r] * dinv : 0.f) - dq[r]);
+                        pr[r] = kp ? pr[r] : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        pr[r] = fast_exp2(fmaf(sacc[kb][r], c, -lq[r]));
+                        ds[r] = pr[r] * (dpacc[kb][r] - dq[r]);
+                    }
+                }
                 if ((CAUSAL && (qb0 < key0 + 31 - wr_ || (WIN && qb0 + 31 > key0 + wl_))) || qb0 + 31 >= N) {
                     // hide queries outside key - wr .. key + wl and rows q >= N: P and dS become 0
                     const int thr = CAUSAL ? key0 + l32 - wr_ - qb0 - 4 * hi : -1;
@@ -361,7 +378,8 @@ void bwd_dkdv2_kernel(BwdParams p) {
                 const int kk = kw0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
                 if (kk < N) {
                     dKh[size_t(kk) * D + db * 32 + l32] = (bf16)(dk[kb][db][r] * p.scale);
-                    dVh[size_t(kk) * D + db * 32 + l32] = (bf16)(dv[kb][db][r]);
+                    dVh[size_t(kk) * D + db * 32 + l32] =
+                        (bf16)(DROP ? dv[kb][db][r] * (256.f / float(256 - p.drop_t8)) : dv[kb][db][r]);
                 }
             }
         }
@@ -735,7 +753,7 @@ struct DqLds {
     static constexpr size_t BYTES = size_t(kDqStages) * STAGE_BYTES;
 };
 
-template <int D, int MASK>
+template <int D, int MASK, bool DROP>
 __global__ __launch_bounds__(kDqWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq2_kernel(BwdParams p) {
     // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
@@ -895,10 +913,20 @@ void bwd_dq2_kernel(BwdParams p) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 float ds[16];
+                uint32_t dy[4];  // dropout keep bytes: dP is dropped and scaled before dS
+                if constexpr (DROP)
+                    drop_bytes_qmajor(dy, wq0 + 32 * rb + l32, kb0, hi, lane, uint32_t(b * p.Hq + h), p.drop_off,
+                                      p.drop_k0, p.drop_k1);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float pr = fast_exp2(fmaf(s[rb][r], c, -lse2[rb]));
-                    ds[r] = pr * (dpt[rb][r] - drow[rb]);
+                    if constexpr (DROP) {
+                        const float dpd = drop_keep(dy, r, p.drop_t8) ? dpt[rb][r] * (256.f / float(256 - p.drop_t8))
+                                                                       : 0.f;
+                        ds[r] = pr * (dpd - drow[rb]);
+                    } else {
+                        ds[r] = pr * (dpt[rb][r] - drow[rb]);
+                    }
                 }
                 if ((CAUSAL && (kb0 + 31 > wq0 + 32 * rb + wr_ || (WIN && kb0 < wq0 + 32 * rb + 31 - wl_))) ||
                     kb0 + 31 >= N) {
@@ -954,7 +982,7 @@ void bwd_dq2_kernel(BwdParams p) {
     }
 }
 
-template <int D, int MASK>
+template <int D, int MASK, bool DROP = false>
 hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     // 1. D_i = dO_i . O_i
     // Every query row of every head: [B, Hq, N] rows, or [Hq, total] packed.
@@ -967,7 +995,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
 
     // 2. dK, dV
     constexpr size_t list_bytes = MASK == 3 ? size_t(kSparseListCap + 1) * sizeof(int) : 0;
-    if constexpr (D == 128 || MASK == 3) {
+    if constexpr ((D == 128 || MASK == 3) && !DROP) {
         auto kern = bwd_dkdv3_kernel<D, MASK>;
         constexpr size_t lds = Dk3Lds<D>::BYTES + list_bytes;
         static DeviceOnce attr;
@@ -977,7 +1005,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
-        auto kern = bwd_dkdv2_kernel<D, MASK>;
+        auto kern = bwd_dkdv2_kernel<D, MASK, DROP>;
         constexpr size_t lds = DkLds<D>::BYTES;
         static DeviceOnce attr;
         if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
@@ -988,7 +1016,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
     }
     // 3. dQ
     {
-        auto kern = bwd_dq2_kernel<D, MASK>;
+        auto kern = bwd_dq2_kernel<D, MASK, DROP>;
         constexpr size_t lds = DqLds<D>::BYTES + list_bytes;
         static DeviceOnce attr;
         if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
@@ -1005,6 +1033,12 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
 hipError_t launch_bwd_bf16(BwdParams p, int d, int causal, hipStream_t stream) {
     // 0: no mask, 1: causal, 2: a general window, 3: block map (and window)
     const int mk = p.bmask != nullptr ? 3 : !causal ? 0 : (p.wl >= kUnbounded && p.wr == 0) ? 1 : 2;
+    if (p.drop_t8 > 0) {
+        // dropout: fixed-length batches, no window or map (the entry point checks)
+        if (d == 64) return mk == 0 ? launch_bwd_t<64, 0, true>(p, stream) : launch_bwd_t<64, 1, true>(p, stream);
+        if (d == 128) return mk == 0 ? launch_bwd_t<128, 0, true>(p, stream) : launch_bwd_t<128, 1, true>(p, stream);
+        return hipErrorNotSupported;
+    }
     switch (d) {
         case 64:
             return mk == 0   ? launch_bwd_t<64, 0>(p, stream)

@@ -120,6 +120,107 @@ __device__ __forceinline__ int compact_tiles(int* list, int n, int lane, F tag) 
     return count;
 }
 
+// ---------------------------------------------------------------------------
+// Dropout bits.  Philox-4x32 with 10 rounds (J. K. Salmon, M. A. Moraes,
+// R. O. Dror, D. E. Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC 2011): per round the counter words 0 and 2 are multiplied (full 64-bit
+// products) by 0xD2511F53 and 0xCD9E8D57, the new counter is
+// (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0), and the key is bumped by
+// (0x9E3779B9, 0xBB67AE85) between rounds.
+// One call gives the 16 keep bytes of a 4 x 4 block of (query, key):
+// counter (key / 4, query / 4, batch * H_q + head, offset), word q % 4 is
+// the block's query row, byte k % 4 of it the key.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = uint64_t(0xD2511F53u) * c0;
+        const uint64_t p1 = uint64_t(0xCD9E8D57u) * c2;
+        c0 = uint32_t(p1 >> 32) ^ c1 ^ k0;
+        c1 = uint32_t(p1);
+        c2 = uint32_t(p0 >> 32) ^ c3 ^ k1;
+        c3 = uint32_t(p0);
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return u32x4{c0, c1, c2, c3};
+}
+
+// In every group of 4 lanes (l % 4 = s), lane s ends with x[g] = the input
+// x[s] of lane g: a 4 x 4 transpose of words over the lane quad, in two
+// exchanges with the lanes s ^ 2 and s ^ 1 (DPP quad permutations).
+__device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int lane) {
+    const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
+    {
+        const uint32_t s0 = b1 ? x[0] : x[2], s1 = b1 ? x[1] : x[3];
+        const uint32_t r0 = uint32_t(__builtin_amdgcn_mov_dpp(int(s0), 0x4E, 0xF, 0xF, false));  // lanes [2,3,0,1]
+        const uint32_t r1 = uint32_t(__builtin_amdgcn_mov_dpp(int(s1), 0x4E, 0xF, 0xF, false));
+        if (b1) {
+            x[0] = r0;
+            x[1] = r1;
+        } else {
+            x[2] = r0;
+            x[3] = r1;
+        }
+    }
+    {
+        const uint32_t s0 = b0 ? x[0] : x[1], s1 = b0 ? x[2] : x[3];
+        const uint32_t r0 = uint32_t(__builtin_amdgcn_mov_dpp(int(s0), 0xB1, 0xF, 0xF, false));  // lanes [1,0,3,2]
+        const uint32_t r1 = uint32_t(__builtin_amdgcn_mov_dpp(int(s1), 0xB1, 0xF, 0xF, false));
+        if (b0) {
+            x[0] = r0;
+            x[2] = r1;
+        } else {
+            x[1] = r0;
+            x[3] = r1;
+        }
+    }
+}
+
+// Keep bytes for the score layout with one query per lane (S^T = K Q^T:
+// lane query `q`, register r = key kb0 + 8 (r / 4) + 4 hi + r % 4, kb0 a
+// multiple of 32, the lane quad holding queries 4 (q / 4) .. +3): on return
+// byte t of y[g] is the byte of (q, kb0 + 8 g + 4 hi + t).  Each lane of a
+// quad draws one key group's block, the quad transpose hands every lane its
+// own query row of all four.
+__device__ __forceinline__ void drop_bytes_qmajor(uint32_t (&y)[4], int q, int kb0, int hi, int lane, uint32_t bh,
+                                                  uint32_t off, uint32_t k0, uint32_t k1) {
+    const int s = lane & 3;
+    const u32x4 w = philox4x32_10(uint32_t(kb0 + 8 * s + 4 * hi) >> 2, uint32_t(q) >> 2, bh, off, k0, k1);
+    y[0] = w[0];
+    y[1] = w[1];
+    y[2] = w[2];
+    y[3] = w[3];
+    quad_transpose(y, lane);
+}
+
+// Keep bytes for the score layout with one key per lane (S = Q K^T: lane
+// key `k`, register r = query qb0 + 8 (r / 4) + 4 hi + r % 4, qb0 a multiple
+// of 32, the lane quad holding keys 4 (k / 4) .. +3): on return byte t of
+// y[g] is the byte of (qb0 + 8 g + 4 hi + t, k).  Each lane draws one query
+// group's block, regroups its bytes by key (byte d of word t -> byte t of
+// word d, v_perm), and the quad transpose hands every lane its key's bytes.
+__device__ __forceinline__ void drop_bytes_kmajor(uint32_t (&y)[4], int k, int qb0, int hi, int lane, uint32_t bh,
+                                                  uint32_t off, uint32_t k0, uint32_t k1) {
+    const int s = lane & 3;
+    const u32x4 w = philox4x32_10(uint32_t(k) >> 2, uint32_t(qb0 + 8 * s + 4 * hi) >> 2, bh, off, k0, k1);
+    const uint32_t a_lo = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
+    const uint32_t a_hi = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
+    const uint32_t b_lo = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t b_hi = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    y[0] = __builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u);  // byte 0 of w0..w3
+    y[1] = __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u);  // byte 1
+    y[2] = __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u);  // byte 2
+    y[3] = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);  // byte 3
+    quad_transpose(y, lane);
+}
+
+// Byte t of word y[g] >= the threshold: element r = 4 g + t is kept.
+__device__ __forceinline__ bool drop_keep(const uint32_t (&y)[4], int r, int t8) {
+    return int((y[r >> 2] >> (8 * (r & 3))) & 0xFFu) >= t8;
+}
+
 // Transposing 8-byte LDS read (see the layout note at the top).
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* __restrict__ p) {
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;

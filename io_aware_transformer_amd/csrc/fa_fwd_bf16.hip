@@ -387,7 +387,7 @@ __device__ __forceinline__ void wait_vmem_at_most(int n_groups) {
     }
 }
 
-template <int D, int MASK>
+template <int D, int MASK, bool DROP>
 __global__ __launch_bounds__(kPPWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(FwdParams p) {
     // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
@@ -649,6 +649,14 @@ void fwd_pp_kernel(FwdParams p) {
                 e[r] = fast_exp2(fmaf(s[kb][r], c, -m));
                 rs += e[r];
             }
+            if constexpr (DROP) {
+                // the row sum keeps every term; only P entering PV is dropped
+                uint32_t y[4];
+                drop_bytes_qmajor(y, qrow, kstart + 32 * kb, hi, lane, uint32_t(b * p.Hq + h), p.drop_off, p.drop_k0,
+                                  p.drop_k1);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) e[r] = drop_keep(y, r, p.drop_t8) ? e[r] : 0.f;
+            }
             pb[kb][0] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
             pb[kb][1] = to_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
         }
@@ -680,8 +688,9 @@ void fwd_pp_kernel(FwdParams p) {
 
     const float lt = half_swap_sum(l);
     // A row that sees no key at all (block-sparse only) has l = 0: O = 0,
-    // LSE = -inf.
-    const float inv = (!SPARSE || lt > 0.f) ? 1.f / lt : 0.f;
+    // LSE = -inf.  Dropout scales the kept terms by 256 / (256 - t8).
+    float inv = (!SPARSE || lt > 0.f) ? 1.f / lt : 0.f;
+    if constexpr (DROP) inv *= 256.f / float(256 - p.drop_t8);
     if (qrow < N) {
         bf16* orow = Oh + size_t(qrow) * D;
 #pragma unroll
@@ -698,9 +707,9 @@ void fwd_pp_kernel(FwdParams p) {
     }
 }
 
-template <int D, int MASK>
+template <int D, int MASK, bool DROP = false>
 hipError_t launch_fwd_pp_t(FwdParams p, hipStream_t stream) {
-    auto kern = fwd_pp_kernel<D, MASK>;
+    auto kern = fwd_pp_kernel<D, MASK, DROP>;
     constexpr size_t lds = pp_lds_bytes<D>() + (MASK == 3 ? size_t(kSparseListCap + 1) * sizeof(int) : 0);
     static DeviceOnce attr;
     const hipError_t e = set_max_dynamic_lds(kern, lds, attr);
@@ -740,6 +749,13 @@ hipError_t launch_fwd_bf16(FwdParams p, int d, int causal, hipStream_t stream) {
     }
     // 0: no mask, 1: causal, 2: a general window, 3: block map (and window)
     const int mk = p.bmask != nullptr ? 3 : !causal ? 0 : (p.wl >= kUnbounded && p.wr == 0) ? 1 : 2;
+    if (p.drop_t8 > 0) {
+        // dropout: fixed-length batches, d = 64 / 128, no window (the entry point checks)
+        if (d == 64) return mk == 0 ? launch_fwd_pp_t<64, 0, true>(p, stream) : launch_fwd_pp_t<64, 1, true>(p, stream);
+        if (d == 128)
+            return mk == 0 ? launch_fwd_pp_t<128, 0, true>(p, stream) : launch_fwd_pp_t<128, 1, true>(p, stream);
+        return hipErrorNotSupported;
+    }
     if (mk == 3) {
         // d = 64 / 128 only (the entry point checks)
         if (d == 64) return launch_fwd_pp_t<64, 3>(p, stream);

@@ -38,6 +38,10 @@ struct FwdParams {
     // (wl, wr) allows it).
     const unsigned char* bmask;
     int nb;
+    // Dropout on P (drop_t8 > 0): element kept when its Philox byte >= drop_t8;
+    // key (drop_k0, drop_k1), counter word 3 drop_off.
+    int drop_t8;
+    uint32_t drop_k0, drop_k1, drop_off;
 };
 
 constexpr int kUnbounded = 1 << 30;
@@ -68,6 +72,8 @@ struct BwdParams {
     int total;
     const unsigned char* bmask;  // block-sparse map, as FwdParams
     int nb;
+    int drop_t8;  // dropout, as FwdParams
+    uint32_t drop_k0, drop_k1, drop_off;
 };
 
 // Split key/value forward parameters.  Q [B, Hq, Nq, d], K/V [B, Hkv, Nk, d]

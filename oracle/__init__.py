@@ -18,7 +18,8 @@ see ``oracle/attention.py``, ``oracle/splitkv.py``, ``oracle/window.py`` and
 ``oracle/varlen.py``, ``oracle/blocksparse.py`` and ``oracle/dropout.py``.
 """
 
-from .dropout import dropout_backward, dropout_forward, dropout_threshold, keep_mask, philox4x32_10
+from .dropout import (dropout_backward, dropout_forward, dropout_head_backward, dropout_head_forward,
+                      dropout_threshold, keep_mask, philox4x32_10)
 from .blocksparse import blocksparse_backward, blocksparse_forward, blocksparse_visible
 from .attention import (
     attention_forward,
@@ -52,6 +53,8 @@ __all__ = [
     "blocksparse_visible",
     "dropout_forward",
     "dropout_backward",
+    "dropout_head_forward",
+    "dropout_head_backward",
     "dropout_threshold",
     "keep_mask",
     "philox4x32_10",

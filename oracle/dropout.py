@@ -42,7 +42,8 @@ import numpy as np
 
 from .attention import _check_shapes, _row_softmax, _scores, kv_head_of
 
-__all__ = ["philox4x32_10", "dropout_threshold", "keep_mask", "dropout_forward", "dropout_backward"]
+__all__ = ["philox4x32_10", "dropout_threshold", "keep_mask", "dropout_head_forward", "dropout_head_backward",
+           "dropout_forward", "dropout_backward"]
 
 _M0, _M1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
 _W0, _W1 = 0x9E3779B9, 0xBB67AE85
@@ -91,20 +92,41 @@ def _unit(q, k, scale, causal, keep, t8):
     return p, pz, m + np.log(l)
 
 
+def dropout_head_forward(q, k, v, scale, causal, p, seed, offset, bh):
+    """One (batch, query head) unit with unit index bh = b * H_q + h:
+    (O [N, d], LSE [N])."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    t8 = dropout_threshold(p)
+    keep = keep_mask(q.shape[0], k.shape[0], bh, p, seed, offset)
+    _, pz, lse = _unit(q, k, scale, causal, keep, t8)
+    return pz @ v, lse
+
+
+def dropout_head_backward(q, k, v, do, scale, causal, p, seed, offset, bh):
+    """Backward of one unit: (dQ, dK, dV) of its query head (dK, dV before
+    the sum over a grouped head's query heads)."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    t8 = dropout_threshold(p)
+    keep = keep_mask(q.shape[0], k.shape[0], bh, p, seed, offset)
+    pr, pz, _ = _unit(q, k, scale, causal, keep, t8)
+    dp = np.where(keep, do @ v.T, 0.0) * (256.0 / (256.0 - t8))
+    d_row = (pr * dp).sum(axis=1)
+    ds = pr * (dp - d_row[:, None])
+    return scale * (ds @ k), scale * (ds.T @ q), pz.T @ do
+
+
 def dropout_forward(Q, K, V, scale, causal, p, seed, offset=0):
     """Q [B, H_q, N, d], K/V [B, H_kv, N, d] -> (O, LSE); LSE without dropout."""
     Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
     B, Hq, Hkv, N, d = _check_shapes(Q, K, V)
-    t8 = dropout_threshold(p)
+    dropout_threshold(p)
     O = np.zeros((B, Hq, N, V.shape[3]))
     LSE = np.zeros((B, Hq, N))
     for b in range(B):
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            keep = keep_mask(N, N, b * Hq + h, p, seed, offset)
-            _, pz, lse = _unit(Q[b, h], K[b, g], scale, causal, keep, t8)
-            O[b, h] = pz @ V[b, g]
-            LSE[b, h] = lse
+            O[b, h], LSE[b, h] = dropout_head_forward(Q[b, h], K[b, g], V[b, g], scale, causal, p, seed, offset,
+                                                      b * Hq + h)
     return O, LSE
 
 
@@ -112,18 +134,14 @@ def dropout_backward(Q, K, V, dO, scale, causal, p, seed, offset=0):
     """Analytic backward of ``dropout_forward`` with the same keep mask."""
     Q, K, V, dO = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, dO))
     B, Hq, Hkv, N, d = _check_shapes(Q, K, V)
-    t8 = dropout_threshold(p)
-    inv = 256.0 / (256.0 - t8)
+    dropout_threshold(p)
     dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
     for b in range(B):
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            keep = keep_mask(N, N, b * Hq + h, p, seed, offset)
-            pr, pz, _ = _unit(Q[b, h], K[b, g], scale, causal, keep, t8)
-            dp = np.where(keep, dO[b, h] @ V[b, g].T, 0.0) * inv
-            d_row = (pr * dp).sum(axis=1)
-            ds = pr * (dp - d_row[:, None])
-            dQ[b, h] = scale * (ds @ K[b, g])
-            dK[b, g] += scale * (ds.T @ Q[b, h])
-            dV[b, g] += pz.T @ dO[b, h]
+            dq, dk, dv = dropout_head_backward(Q[b, h], K[b, g], V[b, g], dO[b, h], scale, causal, p, seed, offset,
+                                               b * Hq + h)
+            dQ[b, h] = dq
+            dK[b, g] += dk
+            dV[b, g] += dv
     return dQ, dK, dV

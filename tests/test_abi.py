@@ -365,3 +365,49 @@ def test_noalloc_limit_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define FA_NOALLOC_MAX_ROWS \(1 << (\d+)\)", text)
     assert m and (1 << int(m.group(1))) == _lib.FA_NOALLOC_MAX_ROWS
+
+
+def fwdd(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125, causal=1,
+             p=0.1, seed=1, off=0, dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_fwd_dropout(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                                      a["d"], a["scale"], a["causal"], a["p"], a["seed"], a["off"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(p=-0.01), "FA_ERR_ARG"),
+    (dict(p=float("nan")), "FA_ERR_ARG"),
+    (dict(p=0.999), "FA_ERR_ARG"),      # rounds to 256 / 256
+    (dict(d=256), "FA_ERR_UNSUPPORTED"),
+    (dict(dtype=_lib.FA_FP32), "FA_ERR_UNSUPPORTED"),
+    (dict(Q=None), "FA_ERR_NULL"),
+    (dict(Hq=3, Hkv=2), "FA_ERR_SHAPE"),
+])
+def test_fwd_dropout_rejects(kw, code):
+    assert fwdd(**kw) == E[code]
+
+
+def test_dropout_largest_probability_accepted():
+    # 255.4 / 256 rounds to t8 = 255: valid (validation reaches the pointers)
+    assert fwdd(p=255.4 / 256, Q=None) == E["FA_ERR_NULL"]
+    assert fwdd(B=0, Q=None) == E["FA_OK"]
+
+
+def fwds(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, mask=FAKE, B=1, Hq=2, Hkv=1, N=300, d=64, scale=0.125,
+             causal=1, dtype=_lib.FA_BF16)
+    a.update(kw)
+    return _lib.load().fa_fwd_blocksparse(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["mask"], a["B"], a["Hq"],
+                                          a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), "FA_ERR_NULL"),
+    (dict(d=256), "FA_ERR_UNSUPPORTED"),
+    (dict(dtype=_lib.FA_FP32), "FA_ERR_UNSUPPORTED"),
+    (dict(N=_lib.FA_SPARSE_MAX_N + 1), "FA_ERR_UNSUPPORTED"),
+    (dict(causal=3), "FA_ERR_ARG"),
+])
+def test_fwd_blocksparse_rejects(kw, code):
+    assert fwds(**kw) == E[code]
