@@ -102,40 +102,99 @@ def pct(x, q):
     return x[min(len(x) - 1, max(0, int(math.ceil(q / 100.0 * len(x))) - 1))]
 
 
-def cpu_baseline(p, passes, budget_s):
-    """Time the fp64 oracle on host cores over (b, h) units of the same
-    workload until ``budget_s`` of CPU work is done (at least one unit)."""
+_CPU_LEG = {}  # inputs and GPU results the CPU leg's forked workers read
+
+
+def _blas_one_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def _oracle_unit(unit):
+    """Worker: the fp64 oracle on one (b, h) unit of the workload, timed, and
+    the max-abs difference of the GPU's outputs for that unit."""
     import numpy as np
 
     import oracle
-    from io_aware_transformer_amd import inputs
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    q, k, v, do = inputs.make(1, 1, 1, p.N, p.d, p.torch_dtype, p.seed, with_grad=True)
-    q, k, v, do = (t[0, 0].float().numpy().astype(np.float64) for t in (q, k, v, do))
-    units = 0
+    b, h = unit
+    d = _CPU_LEG
+    p, passes = d["p"], d["passes"]
+    g = h // (p.Hq // p.Hkv)
+    q, k, v, do = (d[n][b, h if n in ("q", "do") else g] for n in ("q", "k", "v", "do"))
     t0 = time.perf_counter()
-    while True:
-        oracle.head_forward(q, k, v, p.scale, p.causal)
-        if "bwd" in passes:
-            oracle.head_backward(q, k, v, do, p.scale, p.causal)
-        units += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    o, lse = oracle.head_forward(q, k, v, p.scale, p.causal)
+    grads = oracle.head_backward(q, k, v, do, p.scale, p.causal) if "bwd" in passes else None
     dt = time.perf_counter() - t0
+    err = {"O": (float(np.max(np.abs(d["o"][b, h] - o))), float(np.max(np.abs(o)))),
+           "LSE": (float(np.max(np.abs(d["lse"][b, h] - lse))), float(np.max(np.abs(lse))))}
+    if grads is not None:
+        err["dQ"] = (float(np.max(np.abs(d["dq"][b, h] - grads[0]))), float(np.max(np.abs(grads[0]))))
+        if p.Hq == p.Hkv:  # grouped heads: a unit holds only part of dK / dV
+            err["dK"] = (float(np.max(np.abs(d["dk"][b, g] - grads[1]))), float(np.max(np.abs(grads[1]))))
+            err["dV"] = (float(np.max(np.abs(d["dv"][b, g] - grads[2]))), float(np.max(np.abs(grads[2]))))
+    return dt, err
+
+
+def cpu_baseline(p, passes, budget_s, m):
+    """The fp64 oracle timed on the host's cores over (b, h) units of the same
+    workload (the GPU's own inputs), a pool of single-threaded workers (one
+    BLAS thread each, at most 16: this host's share), in rounds of one unit
+    per worker until ``budget_s`` of wall time is spent.  The same units give
+    the GPU outputs' max-abs errors against the oracle (and the oracle's
+    largest magnitudes), per output."""
+    import multiprocessing
+
+    import numpy as np
+
+    t = m["tensors"]
+    f64 = lambda x: x.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    _CPU_LEG.clear()
+    _CPU_LEG.update({"p": p, "passes": passes})
+    for n in ("q", "k", "v", "do", "o", "lse", "dq", "dk", "dv"):
+        if t[n] is not None:
+            _CPU_LEG[n] = f64(t[n])
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    workers = max(1, min(16, cores))
+    # memory: about 8 N x N float64 arrays live per worker
+    mem_per = 8 * 8 * p.N * p.N
+    try:
+        avail = os.sysconf("SC_AVPHYS_PAGES") * os.sysconf("SC_PAGE_SIZE")
+        workers = max(1, min(workers, int(avail * 0.5 // mem_per)))
+    except (ValueError, OSError):  # pragma: no cover
+        avail = None
+    units = m["units"]
+    rng = np.random.default_rng(p.seed)
+    order = [units[i] for i in rng.permutation(len(units))]
+    done, errs = 0, {}
+    t0 = time.perf_counter()
+    with multiprocessing.get_context("fork").Pool(workers, initializer=_blas_one_thread) as pool:
+        while done < len(order) and (done == 0 or time.perf_counter() - t0 < budget_s):
+            for _, e in pool.map(_oracle_unit, order[done:done + workers]):
+                for name, (err, top) in e.items():
+                    a, b = errs.get(name, (0.0, 0.0))
+                    errs[name] = (max(a, err), max(b, top))
+            done += len(order[done:done + workers])
+    dt = time.perf_counter() - t0
+    _CPU_LEG.clear()
     unit_flops = flops(p, passes)[0] / (p.B * p.Hq)
     return {
-        "value": round(units * unit_flops / dt / 1e12, 6),
+        "value": round(done * unit_flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{units} (batch, head) units of N={p.N} d={p.d} ({'+'.join(passes)}) in {dt:.1f} s, "
-                  f"same FLOP count per unit as the GPU line",
+        "sample": f"{done} of {len(units)} (batch, head) units of the workload ({'+'.join(passes)}, N={p.N} "
+                  f"d={p.d}, fp64 numpy) on {workers} single-threaded worker processes in {dt:.1f} s, same FLOP "
+                  f"count per unit as the GPU line",
+        "parity_on_sample": {k: {"max_abs_err": round(v[0], 7), "oracle_max_abs": round(v[1], 5)}
+                             for k, v in errs.items()},
     }
 
 
@@ -392,6 +451,13 @@ def main():
                          "fa_fwd_window / fa_bwd_window; FLOP counted over the visible (query, key) pairs")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="repetitions of the cold-MALL variant (a 512 MB buffer is written before each; 0 disables)")
+    ap.add_argument("--sparse", default=None,
+                    help="band:K or bigbird:K: block-sparse attention (128-position blocks; each query block sees "
+                         "itself and the K-1 blocks before it, bigbird also the first block) through "
+                         "fa_fwd_blocksparse / fa_bwd_blocksparse; FLOP counted over the visible pairs")
+    ap.add_argument("--dropout", default=None, help="P: dropout probability on P through fa_fwd_dropout / "
+                                                    "fa_bwd_dropout (FLOP counted as without dropout)")
+    ap.add_argument("--no-legs", action="store_true", help="do not add the N=8192 leg to the default run")
     args = ap.parse_args()
 
     if args.print_source_hash:
@@ -428,127 +494,283 @@ def main():
         return
     p = inputs.PRESETS[args.preset]
     passes = [x for x in args.passes.split(",") if x]
+    mode = Mode.from_args(args)
+    m = measure_fixed(args, p, passes, mode, dev, cold_reps=args.cold_reps)
+    line = fixed_line(args, p, m, mode)
+    # Long-context leg (the metric spans N = 2K-8K): the default run also
+    # times fwd+bwd at B2 H16 N8192 d128 with the same kernels.
+    if args.preset == "c2" and mode.kind == "dense" and not args.no_legs:
+        m3 = measure_fixed(args, inputs.PRESETS["c3a"], passes, mode, dev, steps=max(3, args.steps // 2),
+                           warmup=max(1, args.warmup // 2), cold_reps=0, sample_clock=False)
+        line["legs"] = {"c3a": leg_summary(inputs.PRESETS["c3a"], m3)}
+    line["clock"] = m["clock"]
+    if args.cpu_seconds > 0 and mode.kind == "dense":
+        line["cpu_baseline"] = cpu_baseline(p, passes, args.cpu_seconds, m)
+    print(json.dumps(line), flush=True)
 
-    window = None
-    if args.window:
-        window = tuple(int(x) for x in args.window.split(","))
-        from io_aware_transformer_amd import bwd_window, fwd_window
 
-        def fwd(q, k, v, scale, causal, out=None, lse=None):  # noqa: F811 -- same call shape as the causal pass
-            return fwd_window(q, k, v, window, scale=scale, out=out, lse=lse)
+class Mode:
+    """Which entry points a fixed-length run times: dense (fa_fwd / fa_bwd),
+    a window, a block map or dropout; and the FLOP it counts."""
 
-        def bwd(q, k, v, o, lse, do, scale, causal, workspace=None):  # noqa: F811
-            return bwd_window(q, k, v, o, lse, do, window, scale=scale, workspace=workspace)
+    def __init__(self, kind="dense", window=None, sparse=None, dropout=None):
+        self.kind, self.window, self.sparse, self.dropout = kind, window, sparse, dropout
 
+    @staticmethod
+    def from_args(args):
+        if args.window:
+            return Mode("window", window=tuple(int(x) for x in args.window.split(",")))
+        if args.sparse:
+            return Mode("sparse", sparse=args.sparse)
+        if args.dropout is not None:
+            return Mode("dropout", dropout=float(args.dropout))
+        return Mode()
+
+    def block_map(self, p):
+        """The block map of --sparse: 'band:K' -- every query block sees itself
+        and the K - 1 blocks before it; 'bigbird:K' -- the band plus the first
+        key block (a global block)."""
+        import numpy as np
+
+        nb = (p.N + 127) // 128
+        kind, _, kk = self.sparse.partition(":")
+        width = int(kk or 4)
+        m = np.zeros((nb, nb), dtype=np.uint8)
+        for i in range(nb):
+            m[i, max(0, i - width + 1):i + 1] = 1
+            if kind == "bigbird":
+                m[i, 0] = 1
+        return m
+
+    def pairs(self, p):
+        """Visible (query, key) pairs of one (b, h) unit, or None for the
+        causal / full convention."""
+        import numpy as np
+
+        if self.kind == "window":
+            return window_pairs(p.N, *self.window)
+        if self.kind == "sparse":
+            m = self.block_map(p)
+            i = np.arange(p.N)
+            vis = m[i[:, None] // 128, i[None, :] // 128] != 0
+            if p.causal:
+                vis &= i[None, :] <= i[:, None]
+            return int(vis.sum())
+        return None
+
+    def describe(self, p):
+        if self.kind == "window":
+            return f"window {self.window[0]},{self.window[1]}"
+        if self.kind == "sparse":
+            return f"block-sparse {self.sparse}{' causal' if p.causal else ''}"
+        if self.kind == "dropout":
+            return f"dropout p={self.dropout}{' causal' if p.causal else ''}"
+        return "causal" if p.causal else "non-causal"
+
+
+def read_sclk_ghz():
+    """Current shader clock of GPU 0 from rocm-smi (a child process), or None."""
+    import re
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except Exception:
+        return None
+    for line in r.stdout.splitlines():
+        if "sclk" in line:
+            mm = re.search(r"\((\d+)\s*Mhz\)", line, re.I)
+            if mm:
+                return int(mm.group(1)) / 1000.0
+    return None
+
+
+def measure_fixed(args, p, passes, mode, dev, steps=None, warmup=None, cold_reps=0, sample_clock=True):
+    """Time `steps` fwd(+bwd) steps of preset p with HIP events on the
+    launching stream; returns the per-step times, the outputs and the inputs
+    (CPU copies of one sample of units for the CPU leg)."""
+    import threading
+
+    import torch
+
+    import io_aware_transformer_amd as fa
+    from io_aware_transformer_amd import FAError, inputs
+
+    steps = steps or args.steps
+    warmup = warmup if warmup is not None else args.warmup
     q, k, v, do = (t.to(dev) for t in inputs.make_preset(p, with_grad=True))
-    o, lse = fwd(q, k, v, scale=p.scale, causal=p.causal)
+    extra = {}
+    if mode.kind == "window":
+        fwd_call = lambda o=None, l=None: fa.fwd_window(q, k, v, mode.window, scale=p.scale, out=o, lse=l)  # noqa
+        bwd_call = lambda o, l, ws: fa.bwd_window(q, k, v, o, l, do, mode.window, scale=p.scale, workspace=ws)  # noqa
+    elif mode.kind == "sparse":
+        bm = torch.from_numpy(mode.block_map(p)).to(dev)
+        extra["block_map_density"] = float(bm.float().mean())
+        fwd_call = lambda o=None, l=None: fa.fwd_blocksparse(q, k, v, bm, scale=p.scale, causal=p.causal,  # noqa
+                                                             out=o, lse=l)
+        bwd_call = lambda o, l, ws: fa.bwd_blocksparse(q, k, v, o, l, do, bm, scale=p.scale,  # noqa
+                                                       causal=p.causal, workspace=ws)
+    elif mode.kind == "dropout":
+        fwd_call = lambda o=None, l=None: fa.fwd_dropout(q, k, v, mode.dropout, 1234, 0, scale=p.scale,  # noqa
+                                                         causal=p.causal, out=o, lse=l)
+        bwd_call = lambda o, l, ws: fa.bwd_dropout(q, k, v, o, l, do, mode.dropout, 1234, 0, scale=p.scale,  # noqa
+                                                   causal=p.causal, workspace=ws)
+    else:
+        fwd_call = lambda o=None, l=None: fa.fwd(q, k, v, scale=p.scale, causal=p.causal, out=o, lse=l)  # noqa
+        bwd_call = lambda o, l, ws: fa.bwd(q, k, v, o, l, do, scale=p.scale, causal=p.causal, workspace=ws)  # noqa
+    o, lse = fwd_call()
+    ws = None
     if "bwd" in passes:
+        ws = torch.empty(max(1, fa.bwd_workspace_size(p.B, p.Hq, p.Hkv, p.N, p.d, q.dtype)), device=dev,
+                         dtype=torch.uint8)
         try:
-            bwd(q, k, v, o, lse, do, scale=p.scale, causal=p.causal)
+            grads = bwd_call(o, lse, ws)
         except FAError as e:
             print(f"backward unavailable ({e}); timing the forward only", file=sys.stderr)
             passes = [x for x in passes if x != "bwd"]
+            grads = None
     torch.cuda.synchronize()
-
-    ws = None
-    if "bwd" in passes:
-        from io_aware_transformer_amd import bwd_workspace_size
-
-        ws = torch.empty(max(1, bwd_workspace_size(p.B, p.Hq, p.Hkv, p.N, p.d, q.dtype)), device=dev,
-                         dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         if "fwd" in passes:
-            fwd(q, k, v, scale=p.scale, causal=p.causal, out=o, lse=lse)
+            fwd_call(o, lse)
         if ev is not None:
             ev[1].record(stream)
         if "bwd" in passes:
-            bwd(q, k, v, o, lse, do, scale=p.scale, causal=p.causal, workspace=ws)
+            bwd_call(o, lse, ws)
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+    # Shader clock under this load: rocm-smi (a child process, ~1 s to
+    # answer) samples it while the same steps keep running, untimed.
+    clock = {"nominal_sclk_ghz": 2.4, "sclk_under_load_ghz": None}
+    if sample_clock:
+        sampler = threading.Thread(target=lambda: clock.__setitem__("sclk_under_load_ghz", read_sclk_ghz()),
+                                   daemon=True)
+        sampler.start()
+        t0 = time.perf_counter()
+        while sampler.is_alive() and time.perf_counter() - t0 < 20:
+            for _ in range(5):
+                step()
+            torch.cuda.synchronize()
+        sampler.join(timeout=5)
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    ms_per_step = total_ms / args.steps
-    total_flops, fwd_flops = flops(p, passes)
-    if window is not None:
-        fwd_flops = 4.0 * p.B * p.Hq * p.d * window_pairs(p.N, *window)
-        total_flops = fwd_flops * (("fwd" in passes) + 2.5 * ("bwd" in passes))
-    value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    def med(x):
-        x = sorted(x)
-        return x[len(x) // 2]
-
-    # Cold-MALL variant: a 512 MB buffer write before every repetition evicts
-    # the inputs from the L2 and MALL, so each pass starts from HBM.
     cold = None
-    if args.cold_reps > 0:
+    if cold_reps > 0:
+        # a 512 MB buffer write before every repetition evicts the inputs
+        # from the L2 and MALL, so each pass starts from HBM
         buf = torch.empty(COLD_BUFFER_BYTES // 4, device=dev, dtype=torch.float32)
-        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_reps)]
-        for i in range(args.cold_reps):
+        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(cold_reps)]
+        for i in range(cold_reps):
             buf.fill_(float(i))
             step(cevs[i])
         torch.cuda.synchronize()
-        cold = {"reps": args.cold_reps, "evict_bytes": COLD_BUFFER_BYTES,
+        cold = {"reps": cold_reps, "evict_bytes": COLD_BUFFER_BYTES,
                 "fwd_ms_median": round(med([e[0].elapsed_time(e[1]) for e in cevs]), 5) if "fwd" in passes else None,
                 "bwd_ms_median": round(med([e[1].elapsed_time(e[2]) for e in cevs]), 5) if "bwd" in passes else None}
         del buf
+    # one sample of units for the CPU leg: (b, h) in the order the leg takes them
+    units = [(b, h) for b in range(p.B) for h in range(p.Hq)]
+    return {"passes": passes, "total_ms": total_ms, "steps": steps, "warmup": warmup, "fwd_ms": fwd_ms,
+            "bwd_ms": bwd_ms, "cold": cold, "clock": clock, "extra": extra, "units": units,
+            "tensors": {"q": q, "k": k, "v": v, "do": do, "o": o, "lse": lse,
+                        "dq": grads[0] if "bwd" in passes else None, "dk": grads[1] if "bwd" in passes else None,
+                        "dv": grads[2] if "bwd" in passes else None}}
 
+
+def med(x):
+    x = sorted(x)
+    return x[len(x) // 2]
+
+
+def fixed_flops(p, passes, mode):
+    total, fwd_flops = flops(p, passes)
+    pairs = mode.pairs(p)
+    if pairs is not None:
+        fwd_flops = 4.0 * p.B * p.Hq * p.d * pairs
+        total = fwd_flops * (("fwd" in passes) + 2.5 * ("bwd" in passes))
+    return total, fwd_flops
+
+
+def leg_summary(p, m):
+    passes = m["passes"]
+    total_flops, fwd_flops = fixed_flops(p, passes, Mode())
+    fa_ = sum(m["fwd_ms"]) / len(m["fwd_ms"])
+    ba = sum(m["bwd_ms"]) / len(m["bwd_ms"])
+    ms = m["total_ms"] / m["steps"]
+    out = {"workload": f"{p.name}: {'+'.join(passes)} {p.dtype} {'causal' if p.causal else 'non-causal'} "
+                       f"B={p.B} H_q={p.Hq} H_kv={p.Hkv} N={p.N} d={p.d}",
+           "steps": m["steps"], "ms_per_step": round(ms, 5),
+           "tflops": round(total_flops / (ms * 1e-3) / 1e12, 2),
+           "fwd_tflops": round(fwd_flops / (fa_ * 1e-3) / 1e12, 2),
+           "fwd_frac": round(fwd_flops / (fa_ * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "fwd_avg_launch_ms": round(fa_, 5)}
+    if "bwd" in passes:
+        out["bwd_tflops"] = round(2.5 * fwd_flops / (ba * 1e-3) / 1e12, 2)
+        out["bwd_frac"] = round(2.5 * fwd_flops / (ba * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        out["bwd_avg_call_ms"] = round(ba, 5)
+    return out
+
+
+def fixed_line(args, p, m, mode):
+    import torch
+
+    passes = m["passes"]
+    total_flops, fwd_flops = fixed_flops(p, passes, mode)
+    ms_per_step = m["total_ms"] / m["steps"]
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    fwd_ms, bwd_ms = m["fwd_ms"], m["bwd_ms"]
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     fwd_tflops = fwd_flops / (fwd_avg * 1e-3) / 1e12 if "fwd" in passes else None
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
     bwd_tflops = 2.5 * fwd_flops / (bwd_avg * 1e-3) / 1e12 if "bwd" in passes else None
-
-    # Roofline of the forward kernel (one launch per fa_fwd call, so HIP
+    dev = torch.device("cuda:0")
+    # Roofline of the forward kernel (one launch per forward call, so HIP
     # events around the call time exactly that kernel), bound by bf16 MFMA
-    # throughput; the backward pass (three kernels per fa_bwd call) is given
-    # as a whole in roofline_bwd.
+    # throughput; the backward (three kernels per call) is given as a whole
+    # in roofline_bwd.
     fwd_kernel = ("fwd_pp_kernel" if p.d in (64, 128) else "fwd_bf16_kernel") if p.dtype == "bf16" else "fwd_f32_kernel"
+    mask_id = {"dense": 1 if p.causal else 0, "window": 2, "sparse": 3, "dropout": 1 if p.causal else 0}[mode.kind]
     roofline = {
         "bound": "mfma",
-        "kernel": "%s<%d,%s>" % (fwd_kernel, p.d, "true" if p.causal else "false"),
+        "kernel": "%s<%d,%d%s>" % (fwd_kernel, p.d, mask_id, ",dropout" if mode.kind == "dropout" else ""),
         "achieved": round(fwd_tflops, 2) if fwd_tflops else None,
         "peak": round(PEAK_BF16_TFLOPS, 1),
         "unit": "TFLOP/s",
         "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
-        "traffic": None,  # filled from --traffic-json when counters were taken
+        "traffic": None,  # filled from --traffic-json / stored counter data when they match the sources
         "avg_launch_ms": round(fwd_avg, 5),
         "alg_hbm_gbs": round(alg_bytes_fwd(p) / (fwd_avg * 1e-3) / 1e9, 1),
     }
     roofline_bwd = None
     if "bwd" in passes:
-        roofline_bwd = {
-            "bound": "mfma",
-            "kernels": "bwd_pre + bwd_dkdv + bwd_dq (one fa_bwd call)",
-            "achieved": round(bwd_tflops, 2),
-            "peak": round(PEAK_BF16_TFLOPS, 1),
-            "unit": "TFLOP/s",
-            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
-            "avg_call_ms": round(bwd_avg, 5),
-            "flop_convention": "2.5 x forward",
-        }
+        roofline_bwd = {"bound": "mfma", "kernels": "bwd_pre + bwd_dkdv + bwd_dq (one backward call)",
+                        "achieved": round(bwd_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                        "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "avg_call_ms": round(bwd_avg, 5),
+                        "flop_convention": "2.5 x forward"}
     t = None
     if args.traffic_json:
         with open(args.traffic_json) as f:
             t = json.load(f)
-    elif p.dtype == "bf16":
+    elif p.dtype == "bf16" and mode.kind == "dense":
         t = stored_traffic(p)
     if t is not None:
         roofline["traffic"] = t["fetch_bytes"] + t["write_bytes"]
@@ -557,7 +779,8 @@ def main():
                                       "write_factor": t.get("write_factor"), "source": t.get("source", "")}
     if "fwd" in passes and p.dtype == "bf16":
         # transcendental co-bound: the forward's exponentials at the measured v_exp_f32 rate
-        n_exp = exp_count(p) if window is None else float(p.B) * p.Hq * window_pairs(p.N, *window)
+        pairs = mode.pairs(p)
+        n_exp = exp_count(p) if pairs is None else float(p.B) * p.Hq * pairs
         roofline["exp_bound_ms"] = round(n_exp / EXP_RATE * 1e3, 5)
         roofline["exp_bound_frac_of_launch"] = round(n_exp / EXP_RATE * 1e3 / fwd_avg, 4)
     line = {
@@ -565,8 +788,8 @@ def main():
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": m["steps"],
+        "warmup": m["warmup"],
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -574,10 +797,10 @@ def main():
         "dtype": p.dtype,
         "data": "synthetic: seeded N(0,1) Q, K, V, dO rounded to bf16, resident in HBM",
         "config": {
-            "workload": f"{p.name}: {'+'.join(passes)} {p.dtype} "
-                        f"{('window ' + args.window) if window else ('causal' if p.causal else 'non-causal')} "
+            "workload": f"{p.name}: {'+'.join(passes)} {p.dtype} {mode.describe(p)} "
                         f"attention B={p.B} H_q={p.Hq} H_kv={p.Hkv} N={p.N} d={p.d}",
-            "window": list(window) if window else None,
+            "window": list(mode.window) if mode.window else None,
+            "block_map": mode.sparse, "dropout": mode.dropout,
             "B": p.B, "H_q": p.Hq, "H_kv": p.Hkv, "N": p.N, "d": p.d, "causal": p.causal,
             "passes": passes, "parallelism": "single GPU",
         },
@@ -588,15 +811,15 @@ def main():
         "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
         "bwd_ms_median": round(med(bwd_ms), 5) if "bwd" in passes else None,
         "bwd_ms_p10_p90": [round(pct(bwd_ms, 10), 5), round(pct(bwd_ms, 90), 5)] if "bwd" in passes else None,
-        "cold_mall": cold,
+        "cold_mall": m["cold"],
         "peak_inputs": {"cus": torch.cuda.get_device_properties(dev).multi_processor_count, "sclk_ghz": 2.4,
                         "flop_per_clk_per_cu": 4096},
         "roofline": roofline,
         "roofline_bwd": roofline_bwd,
     }
-    if args.cpu_seconds > 0 and window is None:
-        line["cpu_baseline"] = cpu_baseline(p, passes, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    if m["extra"]:
+        line["config"].update(m["extra"])
+    return line
 
 
 if __name__ == "__main__":
