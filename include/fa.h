@@ -108,7 +108,14 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for these
  * sizes (0 when there is nothing to do).  The workspace holds the per-row
- * term D_i = sum_c dO[i][c] O[i][c] (float32 [B,H_q,N]).
+ * term D_i = sum_c dO[i][c] O[i][c] (float32 [B,H_q,N]), rounded up to 256
+ * bytes.  For bf16 with grouped heads (H_q > H_kv) whose dK/dV grid would
+ * leave compute units idle, each key/value head's query heads are split
+ * over S workgroups (S a power of two dividing H_q / H_kv, chosen from the
+ * current device's compute-unit count), and the workspace also holds their
+ * float32 partial dK and dV, 2 x S*B*H_kv*N*d*4 bytes (each rounded up to
+ * 256), summed in slice order.  Query it with the device that will run the
+ * backward current; the same sizes give the same answer on that device.
  */
 size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, int dtype);
 

@@ -120,7 +120,7 @@ int fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, i
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
              void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d,
              float scale, int left, int right, int dtype, void* stream, const int* cu = nullptr, int total = 0,
-             const unsigned char* bmask = nullptr, Drop drop = Drop()) {
+             const unsigned char* bmask = nullptr, Drop drop = Drop(), bool allow_split = true) {
     if (dtype == FA_BF16 && d == 256) return FA_ERR_UNSUPPORTED;
     if (B == 0 || N == 0) return FA_OK;
     if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
@@ -128,7 +128,13 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
         !aligned(LSE, 16) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16))
         return FA_ERR_ALIGN;
     const long long rows = cu != nullptr ? (long long)total : (long long)B * N;
-    if (!workspace || workspace_bytes < fa::bwd_workspace_bytes(H_q, rows)) return FA_ERR_WORKSPACE;
+    // Grouped heads of a fixed-length batch: the query heads of a key/value
+    // head may be split over more dK/dV workgroups, whose float partials
+    // live in the workspace after the D term.
+    const int hsplit = (cu == nullptr && allow_split && dtype == FA_BF16) ? fa::bwd_hsplit(B, H_q, H_kv, N) : 1;
+    const size_t need = hsplit > 1 ? fa::bwd_workspace_bytes_split(B, H_q, H_kv, N, d)
+                                   : fa::bwd_workspace_bytes(H_q, rows);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
     fa::BwdParams p{};
     p.Q = Q;
@@ -141,6 +147,15 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
     p.dK = dK;
     p.dV = dV;
     p.Drow = static_cast<float*>(workspace);
+    p.hsplit = hsplit;
+    if (hsplit > 1) {
+        const size_t dbytes = fa::bwd_workspace_bytes(H_q, rows);
+        const size_t kv_elems = size_t(B) * H_kv * N * d;
+        const size_t part = (size_t(hsplit) * kv_elems * sizeof(float) + 255) / 256 * 256;
+        p.dk_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + dbytes);
+        p.dv_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + dbytes + part);
+        p.part_stride = kv_elems;
+    }
     p.B = B;
     p.Hq = H_q;
     p.Hkv = H_kv;
@@ -263,7 +278,8 @@ int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L
 size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, int dtype) {
     if (validate(B, H_q, H_kv, N, d, 1.0f, 0, dtype) != FA_OK) return 0;
     if (B == 0 || N == 0) return 0;
-    return fa::bwd_workspace_bytes(H_q, (long long)B * N);
+    return dtype == FA_BF16 ? fa::bwd_workspace_bytes_split(B, H_q, H_kv, N, d)
+                            : fa::bwd_workspace_bytes(H_q, (long long)B * N);
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
@@ -289,7 +305,7 @@ int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, c
     void* scratch = fa::noalloc_scratch(e);
     if (scratch == nullptr) return hip_failure(e);
     return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, scratch, fa::kNoAllocScratchBytes, B, H_q, H_kv, N, d, scale,
-                    causal ? -1 : -2, causal ? 0 : -2, dtype, stream);
+                    causal ? -1 : -2, causal ? 0 : -2, dtype, stream, nullptr, 0, nullptr, Drop(), false);
 }
 
 int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,

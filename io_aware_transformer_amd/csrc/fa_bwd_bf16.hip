@@ -42,6 +42,28 @@ size_t bwd_workspace_bytes(int Hq, long long rows) {
     return (d_bytes + 255) / 256 * 256;
 }
 
+int bwd_hsplit(int B, int Hq, int Hkv, int N) {
+    // dK/dV workgroups of 128 keys (the d = 64 kernel takes 256; the split is
+    // sized on 128 so the workspace does not depend on the kernel): aim for
+    // two workgroups per compute unit.
+    const int G = Hq / Hkv;
+    const long long wgs = (long long)((N + 127) / 128) * B * Hkv;
+    const long long want = 2LL * device_cu_count();
+    int s = 1;
+    while (wgs * s < want && G % (2 * s) == 0) s *= 2;
+    return s;
+}
+
+size_t bwd_workspace_bytes_split(int B, int Hq, int Hkv, int N, int d) {
+    size_t bytes = bwd_workspace_bytes(Hq, (long long)B * N);
+    const int s = bwd_hsplit(B, Hq, Hkv, N);
+    if (s > 1) {
+        const size_t part = (size_t(s) * B * Hkv * N * d * sizeof(float) + 255) / 256 * 256;
+        bytes += 2 * part;
+    }
+    return bytes;
+}
+
 // Fixed device buffer of the allocation-free backward (fa_bwd_noalloc): it
 // holds the D_i term in place of a caller workspace.  Every device the
 // library runs on keeps one copy for the life of the process; calls on one
@@ -70,6 +92,8 @@ void* noalloc_scratch(hipError_t& err) {
 
 namespace {
 
+__device__ __forceinline__ f32x4 lds_free_ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
 // ---------------------------------------------------------------- bwd_pre
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
@@ -90,6 +114,23 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O
     if (row < rows && part == 0) Drow[row] = acc;
 }
 
+
+// ---------------------------------------------------------------- dK/dV slice sum
+// dK = sum over the query-head slices of their float partials, in slice
+// order (deterministic), rounded once to bf16; 4 elements per thread.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ dkp, const float* __restrict__ dvp,
+                                                          bf16* __restrict__ dK, bf16* __restrict__ dV, long long n4,
+                                                          int S, size_t stride) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    f32x4 k = lds_free_ld4(dkp + 4 * i), v = lds_free_ld4(dvp + 4 * i);
+    for (int s = 1; s < S; ++s) {
+        k += lds_free_ld4(dkp + s * stride + 4 * i);
+        v += lds_free_ld4(dvp + s * stride + 4 * i);
+    }
+    *reinterpret_cast<bf16x4*>(dK + 4 * i) = bf16x4{(bf16)k[0], (bf16)k[1], (bf16)k[2], (bf16)k[3]};
+    *reinterpret_cast<bf16x4*>(dV + 4 * i) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
 
 // ---------------------------------------------------------------- bwd_dkdv v2
 // One workgroup of 4 waves per (batch, kv head, block of 32*KPW*4 keys); each
@@ -150,11 +191,16 @@ void bwd_dkdv2_kernel(BwdParams p) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const float c = p.scale_log2;
-    const int units = p.B * p.Hkv;
+    // unit = (batch, kv head, slice of its group's query heads)
+    const int S = p.hsplit, Hs = p.Hkv * S;
+    const int units = p.B * Hs;
     const int slot = blockIdx.x / units;
-    const int unit = order_unit(blockIdx.x - slot * units, units, p.Hkv, p.cu != nullptr);
-    const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
+    const int unit = order_unit(blockIdx.x - slot * units, units, Hs, p.cu != nullptr);
+    const int b = unit / Hs, gs = unit - (unit / Hs) * Hs;
+    const int g = gs / S, sl = gs - (gs / S) * S;
     const int G = p.Hq / p.Hkv;
+    const int GS = G / S;            // query heads of this workgroup
+    const int h0 = g * G + sl * GS;  // the first of them
     const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
     const int N = sq.n;
     const int kstart = slot * dk_keys_per_wg<D>();
@@ -193,7 +239,7 @@ void bwd_dkdv2_kernel(BwdParams p) {
     const int qt_first = CAUSAL ? max(0, kstart - wr_) / BQ : 0;
     const int qt_last = WIN ? min(nqt - 1, (kstart + dk_keys_per_wg<D>() - 1 + wl_) / BQ) : nqt - 1;
     const int per_head = qt_last - qt_first + 1;
-    const int iters = G * per_head;
+    const int iters = GS * per_head;
 
     // Per-lane copy sources: piece pi = w + 4 i of the Q (and dO) tile.
     int src_off[PPW];
@@ -204,7 +250,7 @@ void bwd_dkdv2_kernel(BwdParams p) {
         src_off[i] = r * D + e0;
     }
     auto issue = [&](int t) {
-        const int hq = g * G + t / per_head;
+        const int hq = h0 + t / per_head;
         const int q0 = (qt_first + t % per_head) * BQ;
         const size_t row0 = sq.qrow(hq) + q0;
         unsigned char* st = smem_raw + (t % NST) * SB;
@@ -300,7 +346,7 @@ void bwd_dkdv2_kernel(BwdParams p) {
                     // factor is applied to dV at the end); dP = dO V^T is
                     // dropped and scaled before dS.
                     uint32_t dy[4];
-                    drop_bytes_kmajor(dy, key0 + l32, qb0, hi, lane, uint32_t(b * p.Hq + g * G + t / per_head),
+                    drop_bytes_kmajor(dy, key0 + l32, qb0, hi, lane, uint32_t(b * p.Hq + h0 + t / per_head),
                                       p.drop_off, p.drop_k0, p.drop_k1);
                     const float dinv = 256.f / float(256 - p.drop_t8);
 #pragma unroll
@@ -377,9 +423,16 @@ void bwd_dkdv2_kernel(BwdParams p) {
             for (int r = 0; r < 16; ++r) {
                 const int kk = kw0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
                 if (kk < N) {
-                    dKh[size_t(kk) * D + db * 32 + l32] = (bf16)(dk[kb][db][r] * p.scale);
-                    dVh[size_t(kk) * D + db * 32 + l32] =
-                        (bf16)(DROP ? dv[kb][db][r] * (256.f / float(256 - p.drop_t8)) : dv[kb][db][r]);
+                    const float kval = dk[kb][db][r] * p.scale;
+                    const float vval = DROP ? dv[kb][db][r] * (256.f / float(256 - p.drop_t8)) : dv[kb][db][r];
+                    const size_t e = size_t(kk) * D + db * 32 + l32;
+                    if (S == 1) {
+                        dKh[e] = (bf16)kval;
+                        dVh[e] = (bf16)vval;
+                    } else {
+                        p.dk_part[sl * p.part_stride + kvoff + e] = kval;
+                        p.dv_part[sl * p.part_stride + kvoff + e] = vval;
+                    }
                 }
             }
         }
@@ -437,11 +490,16 @@ void bwd_dkdv3_kernel(BwdParams p) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const float c = p.scale_log2;
-    const int units = p.B * p.Hkv;
+    // unit = (batch, kv head, slice of its group's query heads)
+    const int S = p.hsplit, Hs = p.Hkv * S;
+    const int units = p.B * Hs;
     const int slot = blockIdx.x / units;
-    const int unit = order_unit(blockIdx.x - slot * units, units, p.Hkv, p.cu != nullptr);
-    const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
+    const int unit = order_unit(blockIdx.x - slot * units, units, Hs, p.cu != nullptr);
+    const int b = unit / Hs, gs = unit - (unit / Hs) * Hs;
+    const int g = gs / S, sl = gs - (gs / S) * S;
     const int G = p.Hq / p.Hkv;
+    const int GS = G / S;            // query heads of this workgroup
+    const int h0 = g * G + sl * GS;  // the first of them
     const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
     const int N = sq.n;
     const int kstart = slot * kDk3KeysPerWg;
@@ -491,7 +549,7 @@ void bwd_dkdv3_kernel(BwdParams p) {
         __syncthreads();
         per_head = __builtin_amdgcn_readfirstlane(lds_i32(tlist + kSparseListCap));
     }
-    const int iters = G * per_head;  // >= 1 unless a block map hides every query tile
+    const int iters = GS * per_head;  // >= 1 unless a block map hides every query tile
     if (SPARSE && iters == 0) {
         // no query sees these keys: their gradients are zero
         bf16* dKh = static_cast<bf16*>(p.dK) + kvoff;
@@ -502,8 +560,14 @@ void bwd_dkdv3_kernel(BwdParams p) {
             for (int r = 0; r < 16; ++r) {
                 const int kk = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
                 if (kk < N) {
-                    dKh[size_t(kk) * D + db * 32 + l32] = bf16(0.f);
-                    dVh[size_t(kk) * D + db * 32 + l32] = bf16(0.f);
+                    const size_t e = size_t(kk) * D + db * 32 + l32;
+                    if (S == 1) {
+                        dKh[e] = bf16(0.f);
+                        dVh[e] = bf16(0.f);
+                    } else {
+                        p.dk_part[sl * p.part_stride + kvoff + e] = 0.f;
+                        p.dv_part[sl * p.part_stride + kvoff + e] = 0.f;
+                    }
                 }
             }
         return;
@@ -530,7 +594,7 @@ void bwd_dkdv3_kernel(BwdParams p) {
         int last_row;  // rows past N read row N-1 (their results are hidden)
     };
     auto tile_copy = [&](int t) {
-        const int hq = g * G + t / per_head;
+        const int hq = h0 + t / per_head;
         const int q0 = tile_q0(t);
         const size_t row0 = sq.qrow(hq) + q0;
         const uint32_t bytes = uint32_t(N - q0) * uint32_t(D * 2);
@@ -727,8 +791,14 @@ void bwd_dkdv3_kernel(BwdParams p) {
         for (int r = 0; r < 16; ++r) {
             const int kk = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
             if (kk < N) {
-                dKh[size_t(kk) * D + db * 32 + l32] = (bf16)(dk[db][r] * p.scale);
-                dVh[size_t(kk) * D + db * 32 + l32] = (bf16)(dv[db][r]);
+                const size_t e = size_t(kk) * D + db * 32 + l32;
+                if (S == 1) {
+                    dKh[e] = (bf16)(dk[db][r] * p.scale);
+                    dVh[e] = (bf16)(dv[db][r]);
+                } else {
+                    p.dk_part[sl * p.part_stride + kvoff + e] = dk[db][r] * p.scale;
+                    p.dv_part[sl * p.part_stride + kvoff + e] = dv[db][r];
+                }
             }
         }
     }
@@ -1001,7 +1071,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         static DeviceOnce attr;
         if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
         p.nkb = (p.N + kDk3KeysPerWg - 1) / kDk3KeysPerWg;
-        const long long blocks = (long long)p.nkb * p.B * p.Hkv;
+        const long long blocks = (long long)p.nkb * p.B * p.Hkv * p.hsplit;
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
@@ -1010,8 +1080,16 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         static DeviceOnce attr;
         if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
         p.nkb = (p.N + dk_keys_per_wg<D>() - 1) / dk_keys_per_wg<D>();
-        const long long blocks = (long long)p.nkb * p.B * p.Hkv;
+        const long long blocks = (long long)p.nkb * p.B * p.Hkv * p.hsplit;
         hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // 2b. sum of the query-head slices' partials
+    if (p.hsplit > 1) {
+        const long long n4 = (long long)p.B * p.Hkv * p.N * D / 4;
+        hipLaunchKernelGGL(dkdv_reduce_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, stream, p.dk_part,
+                           p.dv_part, static_cast<bf16*>(p.dK), static_cast<bf16*>(p.dV), n4, p.hsplit,
+                           p.part_stride);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 3. dQ

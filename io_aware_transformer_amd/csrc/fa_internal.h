@@ -74,6 +74,15 @@ struct BwdParams {
     int nb;
     int drop_t8;  // dropout, as FwdParams
     uint32_t drop_k0, drop_k1, drop_off;
+    // Grouped heads: the dK/dV kernels split each key/value head's group of
+    // query heads into hsplit slices (workgroups of their own) that write
+    // float partials (dk_part / dv_part + slice * part_stride, indexed like
+    // dK / dV), summed in slice order by a reduction kernel.  1: no split,
+    // results straight to dK / dV.
+    int hsplit;
+    float* dk_part;
+    float* dv_part;
+    size_t part_stride;
 };
 
 // Split key/value forward parameters.  Q [B, Hq, Nq, d], K/V [B, Hkv, Nk, d]
@@ -106,6 +115,11 @@ hipError_t launch_bwd_f32(BwdParams p, int d, int causal, hipStream_t stream);
 // over the batch (B * N for a fixed-length batch, total for packed
 // sequences): the D term only.
 size_t bwd_workspace_bytes(int Hq, long long rows);
+// Query-head slices per key/value head of a fixed-length backward (a power
+// of two dividing H_q / H_kv; 1 unless the dK/dV grid would leave compute
+// units idle), and the workspace bytes including the float partials.
+int bwd_hsplit(int B, int Hq, int Hkv, int N);
+size_t bwd_workspace_bytes_split(int B, int Hq, int Hkv, int N, int d);
 
 // Allocation-free backward: size of the fixed per-device buffer that holds
 // the D_i term (float [B, Hq, N] rows, 256-byte aligned), and its device

@@ -130,6 +130,25 @@ def test_workspace_size_formula():
     assert lib.fa_bwd_workspace_size(1, 3, 2, 3, 64, _lib.FA_BF16) == 0  # invalid shape
 
 
+def test_workspace_size_grouped_split():
+    """Grouped heads add float partial dK / dV per query-head slice when the
+    dK/dV grid (128 keys per workgroup) is under two workgroups per compute
+    unit; 256 compute units stand in for a host without a device."""
+    lib = _lib.load()
+    d_term = lambda B, Hq, N: (B * Hq * N * 4 + 255) // 256 * 256
+    part = lambda S, B, Hkv, N, d: (S * B * Hkv * N * d * 4 + 255) // 256 * 256
+    # B1 Hq16 Hkv1 N8192: 64 workgroups, doubled to 512 at S = 8
+    assert lib.fa_bwd_workspace_size(1, 16, 1, 8192, 128, _lib.FA_BF16) == d_term(1, 16, 8192) + 2 * part(8, 1, 1, 8192, 128)
+    # B2 Hq32 Hkv8 N2048: 256 workgroups, S = 2
+    assert lib.fa_bwd_workspace_size(2, 32, 8, 2048, 64, _lib.FA_BF16) == d_term(2, 32, 2048) + 2 * part(2, 2, 8, 2048, 64)
+    # already 512 workgroups: no split
+    assert lib.fa_bwd_workspace_size(8, 16, 4, 2048, 128, _lib.FA_BF16) == d_term(8, 16, 2048)
+    # S divides the group: G = 3 cannot split
+    assert lib.fa_bwd_workspace_size(1, 3, 1, 1000, 64, _lib.FA_BF16) == d_term(1, 3, 1000)
+    # float32 has no split
+    assert lib.fa_bwd_workspace_size(1, 16, 1, 8192, 128, _lib.FA_FP32) == d_term(1, 16, 8192)
+
+
 def test_bwd_empty_is_noop():
     assert bwd(Q=None, K=None, V=None, O=None, dO=None, LSE=None, dQ=None, dK=None, dV=None, ws=None, N=0) == 0
 

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from gpu_util import REL_BF16, TOL, check_close, check_half_ulp, f64, maxabs, require_gpu
-from io_aware_transformer_amd import FAError, bwd, fwd, inputs
+from io_aware_transformer_amd import FAError, bwd, bwd_workspace_size, fwd, inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -132,10 +132,18 @@ def test_bwd_constant_v_full_size():
         check_close(f64(dv[b, h]), want, 2e-2, None, f"dV[{b},{h}]")
 
 
+def fa_d_term_bytes(B, Hq, N):
+    return (B * Hq * N * 4 + 255) // 256 * 256
+
+
 def test_bwd_deterministic_and_workspace_contents_ignored():
     require_gpu()
+    # grouped heads on a small grid: the query heads of each key/value head
+    # are split over workgroups whose float partials sit in the workspace
     q, k, v, do = inputs.make(2, 8, 2, 777, 64, torch.bfloat16, 12, with_grad=True)
-    ws = torch.full((1 << 20,), 255, dtype=torch.uint8, device="cuda")
+    need = bwd_workspace_size(2, 8, 2, 777, 64)
+    assert need > fa_d_term_bytes(2, 8, 777)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
     a = _gpu_grads(q, k, v, do, 0.125, True)
     b = _gpu_grads(q, k, v, do, 0.125, True, workspace=ws)
     for x, y in zip(a, b):

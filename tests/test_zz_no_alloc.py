@@ -39,8 +39,18 @@ def test_noalloc_equals_bwd_two_calls(d):
         want = bwd(q, k, v, o, lse, do, scale=scale, causal=causal)
         got = _noalloc(q, k, v, o, lse, do, scale, causal)
         torch.cuda.synchronize()
-        for name, x, y in zip(("dQ", "dK", "dV"), got, want):
-            assert torch.equal(x, y), (name, B, Hq, Hkv, N, d)
+        assert torch.equal(got[0], want[0]), ("dQ", B, Hq, Hkv, N, d)
+        for name, x, y in zip(("dK", "dV"), got[1:], want[1:]):
+            if Hq == Hkv:
+                assert torch.equal(x, y), (name, B, Hq, Hkv, N, d)
+            else:
+                # fa_bwd splits a grouped head's query heads over several
+                # workgroups and sums their float partials; the buffer-free
+                # call sums the group in one workgroup.  Both round one float
+                # sum to bf16, so they differ by at most one bf16 ulp.
+                x, y = x.float(), y.float()
+                assert torch.all((x - y).abs() <= 2.0 ** -7 * torch.maximum(x.abs(), y.abs()) + 1e-6), (name, B, Hq,
+                                                                                                     Hkv, N, d)
 
 
 def test_noalloc_rejects_sizes_past_the_buffer():
