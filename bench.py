@@ -747,7 +747,7 @@ def fixed_line(args, p, m, mode):
     # events around the call time exactly that kernel), bound by bf16 MFMA
     # throughput; the backward (three kernels per call) is given as a whole
     # in roofline_bwd.
-    fwd_kernel = ("fwd_pp_kernel" if p.d in (64, 128) else "fwd_bf16_kernel") if p.dtype == "bf16" else "fwd_f32_kernel"
+    fwd_kernel = "fwd_pp_kernel" if p.dtype == "bf16" else "fwd_f32_kernel"
     mask_id = {"dense": 1 if p.causal else 0, "window": 2, "sparse": 3, "dropout": 1 if p.causal else 0}[mode.kind]
     roofline = {
         "bound": "mfma",

@@ -27,11 +27,7 @@ def hipcc():
 
 
 def common_flags():
-    # FA_EXTRA_DEFINES: optional build-time tile-configuration overrides
-    # (e.g. "FA_FWD_CFG128=2"), used for tile sweeps.
-    extra = [f"-D{x}" for x in os.environ.get("FA_EXTRA_DEFINES", "").split() if x]
-    extra += [x for x in os.environ.get("FA_EXTRA_FLAGS", "").split() if x]
-    return [*extra,
+    return [
         f"--offload-arch={ARCH}",
         "-O3",
         "-fPIC",

@@ -11,12 +11,10 @@
 // Work decomposition ("The Future of AI: How FlashAttention Revolutionizes
 // Deep Learning", "FlashAttention-2: Enhanced Performance": parallel over
 // sequence length as well as batch and heads; queries split across warps
-// while keys/values are shared): one workgroup of NW waves per
-// (batch, query head, block of BM = 32*QR*NW query rows); each wave owns
-// QR blocks of 32 query rows; K/V tiles of BN keys are copied global->LDS
-// by the direct-to-LDS load path (no VGPR staging), multi-buffered, and
-// read by every wave.  With QR = 2 every K/V fragment read from LDS feeds two
-// matrix products, halving LDS traffic per FLOP.
+// while keys/values are shared): one workgroup of 8 waves per
+// (batch, query head, block of 256 query rows); each wave owns 32 query
+// rows; K/V tiles of BN keys are copied global->LDS by the direct-to-LDS
+// load path (no VGPR staging) through four stages and read by every wave.
 //
 // Per wave, row block and 32-key block, in the layouts of fa_device.hpp:
 //   S^T (32 keys x 32 queries) = K_blk . Q^T     A = K rows (LDS), B = Q (regs)
@@ -38,31 +36,6 @@ namespace fa {
 
 namespace {
 
-// Tile configuration per head dim: waves per workgroup (each wave owns 32
-// query rows), keys per tile, LDS stages, waves per SIMD the register
-// budget is cut for.
-template <int D>
-struct FwdCfg;
-#ifndef FA_FWD_BN128
-#define FA_FWD_BN128 64
-#endif
-#ifndef FA_FWD_BN64
-#define FA_FWD_BN64 64
-#endif
-#ifndef FA_FWD_NW
-#define FA_FWD_NW 4
-#endif
-template <int NW_, int BN_, int NST_, int WPE_>
-struct FwdCfgT {
-    static constexpr int NW = NW_, BN = BN_, NST = NST_, WPE = WPE_;
-};
-template <>
-struct FwdCfg<64> : FwdCfgT<FA_FWD_NW, FA_FWD_BN64, 2, 2> {};
-template <>
-struct FwdCfg<128> : FwdCfgT<FA_FWD_NW, FA_FWD_BN128, 2, 2> {};
-template <>
-struct FwdCfg<256> : FwdCfgT<4, 32, 2, 1> {};
-
 // Rescale threshold in log2 units.  0: the running max follows the row max
 // exactly (the recurrence as stated; factors of exactly 1 are skipped).
 // > 0: the reference max is only moved when the row max exceeds it by more
@@ -74,24 +47,7 @@ struct FwdCfg<256> : FwdCfgT<4, 32, 2, 1> {};
 // Larger thresholds leave a sharp row's dominant term at 2^delta, rounded to
 // bf16, instead of exactly 1 more often: at 8 the O error of sharp softmaxes
 // grows measurably, at 4 it does not.
-#ifndef FA_FWD_TAU
-#define FA_FWD_TAU 4.0f
-#endif
-constexpr float kTau = FA_FWD_TAU;
-
-// 1: d = 64 / 128 use the ping-pong kernel below; 0: the single-group kernel.
-#ifndef FA_FWD_PP
-#define FA_FWD_PP 1
-#endif
-
-template <int D>
-constexpr int fwd_bm() {
-    return 32 * FwdCfg<D>::NW;
-}
-template <int D>
-constexpr size_t fwd_lds_bytes() {
-    return size_t(FwdCfg<D>::NST) * 2 /*K,V*/ * FwdCfg<D>::BN * D * sizeof(bf16);
-}
+constexpr float kTau = 4.0f;
 
 // Workgroup id -> (query block, batch, head).  Heaviest causal query blocks
 // are issued first; units are ordered over the XCDs by order_unit.
@@ -159,195 +115,8 @@ struct TileCopy {
     }
 };
 
-template <int D, int MASK>
-__global__ __launch_bounds__(FwdCfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE)))
-void fwd_bf16_kernel(FwdParams p) {
-    // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
-    // time); 2: the window (p.wl, p.wr).
-    constexpr bool CAUSAL = MASK != 0;
-    constexpr bool WIN = MASK == 2;  // left bound in use (every wl_ test is guarded by it)
-    const int wl_ = MASK == 2 ? p.wl : kUnbounded;
-    const int wr_ = MASK == 2 ? p.wr : 0;
-    constexpr int NW = FwdCfg<D>::NW, BN = FwdCfg<D>::BN, NST = FwdCfg<D>::NST;
-    constexpr int BM = 32 * NW;
-    constexpr int TILE = BN * D;
-    constexpr int KB = BN / 32;
-    extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
-    bf16* smem = reinterpret_cast<bf16*>(smem_raw);
-
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-    const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const float c = p.scale_log2;  // > 0
-
-    int qb, b, h;
-    fwd_decompose(blockIdx.x, p.B * p.Hq, p.nqb, p.Hq, CAUSAL, p.cu != nullptr, qb, b, h);
-    const int g = h / (p.Hq / p.Hkv);
-    const SeqSpan sq = seq_span(p.cu, p.total, p.Hq, p.Hkv, p.N, b);
-    const int N = sq.n;
-    if (qb * BM >= N) return;  // past the end of a shorter packed sequence (whole workgroup)
-    const size_t qoff = sq.qrow(h) * D;
-    const size_t kvoff = sq.kvrow(g) * D;
-    const bf16* __restrict__ Qh = static_cast<const bf16*>(p.Q) + qoff;
-    const bf16* __restrict__ Kh = static_cast<const bf16*>(p.K) + kvoff;
-    const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
-    bf16* __restrict__ Oh = static_cast<bf16*>(p.O) + qoff;
-
-    const int q0 = qb * BM;
-    const int wq0 = q0 + 32 * w;  // first query row of this wave (uniform)
-    const int wq_last = wq0 + 31;
-    const int qrow = wq0 + l32;   // the query row of this lane
-
-    // Key tiles [kt0, kt0 + ntiles); masked kernels see keys q - wl .. q + wr.
-    const int kend = CAUSAL ? min(N, q0 + BM + wr_) : N;
-    const int kt0 = WIN ? max(0, q0 - wl_) / BN : 0;
-    const int ntiles = (kend + BN - 1) / BN - kt0;
-
-    TileCopy<D, BN, NW> cp;
-    cp.init(w, lane);
-#pragma unroll
-    for (int st = 0; st < NST - 1; ++st)
-        if (st < ntiles) cp.issue(Kh, Vh, smem + st * 2 * TILE, smem + st * 2 * TILE + TILE, (kt0 + st) * BN, N);
-
-    // Q rows of this wave as MFMA B operands: Q[qrow][16cc + 8hi .. +7].
-    // qmode 1 negates (negative scale), 2 zeroes (zero scale).
-    bf16x8 qreg[D / 16];
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) {
-        u32x4 v = u32x4{0, 0, 0, 0};
-        if (qrow < N && p.qmode != 2) v = ld16(Qh + size_t(qrow) * D + 16 * cc + 8 * hi);
-        if (p.qmode == 1) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-        qreg[cc] = as_bf16x8(v);
-    }
-
-    f32x16 o[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    float m = -3.0e38f;  // running (reference) max of c*s; finite floor (rows masked in early tiles)
-    float l = 0.f;        // running sum over this lane's keys (halves merged at the end)
-    const int trow = 4 * hi + ((lane & 15) >> 2);
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    // Row limit for masking: keys above it are hidden (causal and/or past N).
-    const int key_lim = CAUSAL ? min(qrow + wr_, N - 1) : N - 1;
-    const int key_lo = WIN ? qrow - wl_ : 0;
-
-    wait_vmem();
-    __syncthreads();
-
-    for (int kt = 0; kt < ntiles; ++kt) {
-        {
-            const int nt = kt + NST - 1;
-            if (nt < ntiles) {
-                bf16* st = smem + (nt % NST) * 2 * TILE;
-                cp.issue(Kh, Vh, st, st + TILE, (kt0 + nt) * BN, N);
-            }
-        }
-        const bf16* Ks = smem + (kt % NST) * 2 * TILE;
-        const bf16* Vs = Ks + TILE;
-        const int kstart = (kt0 + kt) * BN;
-
-        if (!CAUSAL || (kstart <= wq_last + wr_ && (!WIN || kstart + BN - 1 >= wq0 - wl_))) {
-            // S^T blocks: s[kb][r] = score(key kstart + 32kb + 8(r/4) + 4hi + r%4, query qrow).
-            // The KB accumulation chains are interleaved so consecutive MFMAs are independent.
-            f32x16 s[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-            for (int cc = 0; cc < D / 16; ++cc) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    if (CAUSAL && kstart + 32 * kb > wq_last + wr_) continue;
-                    const bf16x8 a = as_bf16x8(ld16(Ks + kslab_off<BN>(kb * 32 + l32, 16 * cc + 8 * hi)));
-                    s[kb] = mfma_32x32x16(a, qreg[cc], s[kb]);
-                }
-            }
-            const bool need_mask =
-                (CAUSAL && (kstart + BN - 1 > wq0 + wr_ || (WIN && kstart < wq_last - wl_))) || (kstart + BN > N);
-            if (need_mask) {
-                const int lim = key_lim - kstart - 4 * hi;
-                const int lo = key_lo - kstart - 4 * hi;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kk = kb * 32 + 8 * (r >> 2) + (r & 3);
-                        s[kb][r] = (kk > lim || (WIN && kk < lo)) ? -INFINITY : s[kb][r];
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = half_swap_max(mx) * c;
-            // Rescale only when some row of this wave raised its max (by more
-            // than kTau): otherwise every factor exp(m_old - m_new) is exactly
-            // 1 and the multiply is skipped.  The branch is wave-uniform.
-            if (__any(mx > m + kTau)) {
-                const float m_new = fmaxf(m, mx);
-                const float alpha = fast_exp2(m - m_new);
-                m = m_new;
-                l *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-            }
-            bf16x8 pb[KB][2];
-            float rs = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = fast_exp2(fmaf(s[kb][r], c, -m));
-                    s[kb][r] = e;
-                    rs += e;
-                }
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-                    pb[kb][cc] = to_bf16x8(s[kb][8 * cc + 0], s[kb][8 * cc + 1], s[kb][8 * cc + 2], s[kb][8 * cc + 3],
-                                           s[kb][8 * cc + 4], s[kb][8 * cc + 5], s[kb][8 * cc + 6], s[kb][8 * cc + 7]);
-            }
-            l += rs;
-            // O^T += V^T P^T.  Contraction slot (cc, hi, sl) <-> key 32kb + 16cc + 8(sl/4) + 4hi + sl%4.
-            // Consecutive MFMAs update different dim blocks (independent accumulators).
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                if (CAUSAL && kstart + 32 * kb > wq_last + wr_) continue;
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int key = kb * 32 + 16 * cc + trow;
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        const bf16x4 v0 = lds_read_tr(Vs + vslab_off<BN>(key, db * 32 + tcol));
-                        const bf16x4 v1 = lds_read_tr(Vs + vslab_off<BN>(key + 8, db * 32 + tcol));
-                        o[db] = mfma_32x32x16(cat(v0, v1), pb[kb][cc], o[db]);
-                    }
-                }
-            }
-        }
-        wait_vmem();
-        __syncthreads();
-    }
-
-    // Epilogue: O = acc / l (bf16, round to nearest even), LSE = ln2 (m + log2 l).
-    const float lt = half_swap_sum(l);
-    const float inv = 1.f / lt;
-    if (qrow < N) {
-        bf16* orow = Oh + size_t(qrow) * D;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x4 v = bf16x4{(bf16)(o[db][4 * j + 0] * inv), (bf16)(o[db][4 * j + 1] * inv),
-                                        (bf16)(o[db][4 * j + 2] * inv), (bf16)(o[db][4 * j + 3] * inv)};
-                *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * j + 4 * hi) = v;
-            }
-        }
-        if (hi == 0 && p.LSE != nullptr) p.LSE[sq.qrow(h) + qrow] = (m + fast_log2(lt)) * kLn2;
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Ping-pong forward (d = 64, 128).  Two waves share every SIMD; if both ran
+// Ping-pong forward (d = 64, 128, 256).  Two waves share every SIMD; if both ran
 // the same phase (matrix products, then softmax) at the same time, the
 // matrix cores would idle during the softmax.  Here the 8 waves of a
 // workgroup form two groups of 4 (one wave of each group per SIMD) that run
@@ -368,11 +137,16 @@ void fwd_bf16_kernel(FwdParams p) {
 constexpr int kPPWaves = 8;
 constexpr int kPPStages = 4;
 constexpr int kPPBM = 32 * kPPWaves;
-constexpr int kPPBN = 64;
 
+// Keys per tile: 64, or 32 at d = 256 so that four K/V stages fit in LDS
+// (128 KB) and a wave's registers hold O (128), Q (64) and one S block.
+template <int D>
+constexpr int pp_bn() {
+    return D == 256 ? 32 : 64;
+}
 template <int D>
 constexpr size_t pp_lds_bytes() {
-    return size_t(kPPStages) * 2 * kPPBN * D * sizeof(bf16);
+    return size_t(kPPStages) * 2 * pp_bn<D>() * D * sizeof(bf16);
 }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n known only at run time: the
@@ -398,7 +172,7 @@ void fwd_pp_kernel(FwdParams p) {
     constexpr bool SPARSE = MASK == 3;
     const int wl_ = MASK >= 2 ? p.wl : kUnbounded;
     const int wr_ = MASK >= 2 ? p.wr : 0;
-    constexpr int BN = kPPBN;
+    constexpr int BN = pp_bn<D>();
     constexpr int NST = kPPStages;
     constexpr int BM = kPPBM;
     constexpr int TILE = BN * D;
@@ -548,28 +322,32 @@ void fwd_pp_kernel(FwdParams p) {
             // 32kb + 16cc + 8(sl/4) + 4hi + sl%4 of dims db*32 + l32, read
             // transposed from the V slabs of tile j-1.
             const bf16* Vs = smem + ((j - 1) % NST) * 2 * TILE + TILE;
-            bf16x8 fa[D / 32], fb[D / 32];
-            auto load_v = [&](bf16x8(&f)[D / 32], int kb, int cc) {
+            // Chunks of VC output dim blocks, in the order (kb, cc, chunk);
+            // chunk x + 1 is loaded while the MFMAs of chunk x run.
+            constexpr int VC = D / 32 > 4 ? 1 : D / 32;
+            constexpr int NCH = D / 32 / VC;
+            constexpr int X = KB * 2 * NCH;
+            bf16x8 fv[2][VC];
+            auto load_v = [&](bf16x8(&f)[VC], int x) {
+                const int kb = x / (2 * NCH), cc = (x / NCH) & 1, ch = x % NCH;
                 const int key = kb * 32 + 16 * cc + trow;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
+                for (int i = 0; i < VC; ++i) {
+                    const int db = ch * VC + i;
                     const bf16x4 v0 = lds_read_tr(Vs + vslab_off<BN>(key, db * 32 + tcol));
                     const bf16x4 v1 = lds_read_tr(Vs + vslab_off<BN>(key + 8, db * 32 + tcol));
-                    f[db] = cat(v0, v1);
+                    f[i] = cat(v0, v1);
                 }
             };
-            load_v(fa, 0, 0);
+            load_v(fv[0], 0);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                load_v(fb, kb, 1);
+            for (int x = 0; x < X; ++x) {
+                if (x + 1 < X) load_v(fv[(x + 1) & 1], x + 1);
                 __builtin_amdgcn_sched_barrier(0);
+                const int kb = x / (2 * NCH), cc = (x / NCH) & 1, ch = x % NCH;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x16(fa[db], pb[kb][0], o[db]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (kb + 1 < KB) load_v(fa, kb + 1, 0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x16(fb[db], pb[kb][1], o[db]);
+                for (int i = 0; i < VC; ++i)
+                    o[ch * VC + i] = mfma_32x32x16(fv[x & 1][i], pb[kb][cc], o[ch * VC + i]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -720,20 +498,6 @@ hipError_t launch_fwd_pp_t(FwdParams p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int MASK>
-hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
-    auto kern = fwd_bf16_kernel<D, MASK>;
-    constexpr size_t lds = fwd_lds_bytes<D>();
-    static DeviceOnce attr;
-    const hipError_t e = set_max_dynamic_lds(kern, lds, attr);
-    if (e != hipSuccess) return e;
-    constexpr int BM = fwd_bm<D>();
-    p.nqb = (p.N + BM - 1) / BM;
-    const long long blocks = (long long)p.nqb * p.B * p.Hq;
-    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(FwdCfg<D>::NW * 64), lds, stream, p);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_fwd_bf16(FwdParams p, int d, int causal, hipStream_t stream) {
@@ -765,14 +529,9 @@ hipError_t launch_fwd_bf16(FwdParams p, int d, int causal, hipStream_t stream) {
 #define FA_FWD_DISPATCH(L, DD) \
     (mk == 0 ? L<DD, 0>(p, stream) : mk == 1 ? L<DD, 1>(p, stream) : L<DD, 2>(p, stream))
     switch (d) {
-#if FA_FWD_PP
         case 64: return FA_FWD_DISPATCH(launch_fwd_pp_t, 64);
         case 128: return FA_FWD_DISPATCH(launch_fwd_pp_t, 128);
-#else
-        case 64: return FA_FWD_DISPATCH(launch_fwd_bf16_t, 64);
-        case 128: return FA_FWD_DISPATCH(launch_fwd_bf16_t, 128);
-#endif
-        case 256: return FA_FWD_DISPATCH(launch_fwd_bf16_t, 256);
+        case 256: return FA_FWD_DISPATCH(launch_fwd_pp_t, 256);
         default: return hipErrorInvalidValue;
     }
 #undef FA_FWD_DISPATCH
