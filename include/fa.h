@@ -98,7 +98,8 @@ enum fa_status {
  *                                                    NULL when not wanted
  *   B >= 0, N >= 0 (B == 0 or N == 0: nothing to do, returns FA_OK and
  *   pointers may be NULL), 1 <= H_kv <= H_q <= FA_MAX_HEADS, H_q % H_kv == 0,
- *   N <= FA_MAX_N, d in {64, 128, 256}, causal in {0, 1}, scale finite.
+ *   N <= FA_MAX_N, d in {64, 128, 256}, causal in {0, 1}, scale finite with
+ *   |scale| * log2(e) finite in float (|scale| < 2.35e38; else FA_ERR_ARG).
  *   N needs no relation to any tile size.  All pointers 16-byte aligned.
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -341,7 +342,7 @@ size_t fa_fwd_split_workspace_size(int B, int H_q, int H_kv, int N_q, int N_k, i
  *   workspace          at least fa_fwd_split_workspace_size(...) bytes,
  *                      256-byte aligned; contents on entry are ignored
  *   B >= 0, N_q >= 0 (B == 0 or N_q == 0: nothing to do, FA_OK), N_k >= 1,
- *   N_q, N_k <= FA_MAX_N, heads as fa_fwd, causal in {0, 1}, scale finite.
+ *   N_q, N_k <= FA_MAX_N, heads as fa_fwd, causal in {0, 1}, scale as fa_fwd.
  *   dtype FA_BF16 and d in {64, 128}; other valid combinations return
  *   FA_ERR_UNSUPPORTED.
  */

@@ -17,6 +17,12 @@ int hip_failure(hipError_t e) {
     return FA_ERR_HIP;
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// The kernels work with scale * log2(e): a finite scale whose product
+// overflows (|scale| above about 2.36e38) is rejected with the non-finite ones.
+bool scale_ok(float scale) { return std::isfinite(scale) && std::isfinite(scale * kLog2e); }
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Shape / scalar checks shared by fa_fwd and fa_bwd.
@@ -26,14 +32,12 @@ int validate(int B, int Hq, int Hkv, int N, int d, float scale, int causal, int 
     if (Hq < 1 || Hkv < 1 || Hq > FA_MAX_HEADS || Hkv > Hq || Hq % Hkv != 0) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
-    if (!std::isfinite(scale)) return FA_ERR_ARG;
+    if (!scale_ok(scale)) return FA_ERR_ARG;
     // Grid bound: query blocks of 32 rows at the finest, times batch x heads.
-    const long long blocks = ((long long)N + 31) / 32 * (long long)B * (long long)Hq;
+    const long long blocks = fa::sat_mul(fa::sat_mul(((long long)N + 31) / 32, B), Hq);
     if (blocks > (long long)INT_MAX) return FA_ERR_SHAPE;
     return FA_OK;
 }
-
-constexpr float kLog2e = 1.4426950408889634f;
 
 // Checks of the split forward: N_q queries against N_k keys.
 int validate_split(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, int splits) {
@@ -42,7 +46,7 @@ int validate_split(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, i
     if (Hq < 1 || Hkv < 1 || Hq > FA_MAX_HEADS || Hkv > Hq || Hq % Hkv != 0) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
-    if (!std::isfinite(scale)) return FA_ERR_ARG;
+    if (!scale_ok(scale)) return FA_ERR_ARG;
     if (splits < 0 || splits > FA_MAX_SPLITS) return FA_ERR_ARG;
     if (B > 0 && Nq > 0 && Nk == 0) return FA_ERR_SHAPE;  // attention over no keys is undefined
     return FA_OK;
@@ -195,8 +199,8 @@ int validate_varlen(const int* cu, int batch, int total, int max_seqlen, bool& w
 
 bool split_grid_ok(int B, int Hq, int Hkv, int Nq, int parts) {
     const long long rows = (long long)(Hq / Hkv) * Nq;
-    const long long blocks = (long long)B * Hkv * ((rows + 31) / 32) * parts;  // at one wave per workgroup
-    const long long merge_rows = (long long)B * Hq * Nq;
+    const long long blocks = fa::sat_mul(fa::sat_mul(fa::sat_mul(B, Hkv), (rows + 31) / 32), parts);  // one wave each
+    const long long merge_rows = fa::sat_mul(fa::sat_mul(B, Hq), Nq);
     return blocks <= (long long)INT_MAX && merge_rows <= (long long)INT_MAX * 4;
 }
 

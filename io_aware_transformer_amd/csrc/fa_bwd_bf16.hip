@@ -37,33 +37,6 @@
 
 namespace fa {
 
-size_t bwd_workspace_bytes(int Hq, long long rows) {
-    const size_t d_bytes = size_t(Hq) * size_t(rows) * sizeof(float);
-    return (d_bytes + 255) / 256 * 256;
-}
-
-int bwd_hsplit(int B, int Hq, int Hkv, int N) {
-    // dK/dV workgroups of 128 keys (the d = 64 kernel takes 256; the split is
-    // sized on 128 so the workspace does not depend on the kernel): aim for
-    // two workgroups per compute unit.
-    const int G = Hq / Hkv;
-    const long long wgs = (long long)((N + 127) / 128) * B * Hkv;
-    const long long want = 2LL * device_cu_count();
-    int s = 1;
-    while (wgs * s < want && G % (2 * s) == 0) s *= 2;
-    return s;
-}
-
-size_t bwd_workspace_bytes_split(int B, int Hq, int Hkv, int N, int d) {
-    size_t bytes = bwd_workspace_bytes(Hq, (long long)B * N);
-    const int s = bwd_hsplit(B, Hq, Hkv, N);
-    if (s > 1) {
-        const size_t part = (size_t(s) * B * Hkv * N * d * sizeof(float) + 255) / 256 * 256;
-        bytes += 2 * part;
-    }
-    return bytes;
-}
-
 // Fixed device buffer of the allocation-free backward (fa_bwd_noalloc): it
 // holds the D_i term in place of a caller workspace.  Every device the
 // library runs on keeps one copy for the life of the process; calls on one

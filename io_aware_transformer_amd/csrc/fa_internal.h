@@ -133,9 +133,19 @@ void* noalloc_scratch(hipError_t& err);
 hipError_t launch_fwd_split_bf16(SplitParams p, int d, int causal, hipStream_t stream);
 hipError_t launch_lse_merge(const float* Opart, const float* LSEpart, int parts, long long rows, int d, void* O,
                             float* LSE, int out_bf16, hipStream_t stream);
+// Keys per tile of the split forward and its waves per workgroup.
+constexpr int kSplitBN = 32;
+constexpr int split_waves(int d) { return d == 64 ? 4 : 3; }
 int split_parts_default(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 int split_chunk(int Nk, int parts);
 size_t split_workspace_bytes(int B, int Hq, int Nq, int d, int parts);
+
+// Product of non-negative sizes, saturated at LLONG_MAX instead of
+// overflowing (limits are then compared against the saturated value).
+inline long long sat_mul(long long a, long long b) {
+    long long r;
+    return __builtin_mul_overflow(a, b, &r) ? 0x7FFFFFFFFFFFFFFFLL : r;
+}
 
 // Host state shared by every call: per-device flags and a per-device cache
 // of the compute-unit count, both filled once and safe to use from several

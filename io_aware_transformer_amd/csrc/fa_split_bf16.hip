@@ -37,7 +37,6 @@ namespace fa {
 
 namespace {
 
-constexpr int kSplitBN = 32;  // keys per tile
 
 // Waves per workgroup (independent of each other) and LDS stages per wave:
 // three stages keep two tiles in flight while one is computed, which the
@@ -47,11 +46,11 @@ template <int D>
 struct SplitCfg;
 template <>
 struct SplitCfg<64> {
-    static constexpr int WAVES = 4, STAGES = 3;
+    static constexpr int WAVES = split_waves(64), STAGES = 3;
 };
 template <>
 struct SplitCfg<128> {
-    static constexpr int WAVES = 3, STAGES = 3;
+    static constexpr int WAVES = split_waves(128), STAGES = 3;
 };
 
 template <int D>
@@ -326,31 +325,6 @@ hipError_t launch_merge_t(const float* Op, const float* Lp, int parts, long long
 }
 
 }  // namespace
-
-int split_chunk(int Nk, int parts) {
-    const int per = (Nk + parts - 1) / parts;
-    return (per + kSplitBN - 1) / kSplitBN * kSplitBN;
-}
-
-int split_parts_default(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
-    // One workgroup per compute unit (SplitCfg waves each: the LDS holds
-    // one), with at least four 32-key tiles per part.
-    const int nw = d == 64 ? SplitCfg<64>::WAVES : SplitCfg<128>::WAVES;
-    const long long rows = (long long)(Hq / Hkv) * Nq;
-    const long long waves = (long long)B * Hkv * ((rows + 31) / 32);
-    long long parts = ((long long)device_cu_count() * nw + waves - 1) / waves;
-    const long long max_parts = ((long long)Nk + 4 * kSplitBN - 1) / (4 * kSplitBN);
-    if (parts > max_parts) parts = max_parts;
-    if (parts < 1) parts = 1;
-    return int(parts);
-}
-
-size_t split_workspace_bytes(int B, int Hq, int Nq, int d, int parts) {
-    const size_t rows = size_t(B) * Hq * Nq;
-    const size_t o = size_t(parts) * rows * d * sizeof(float);
-    const size_t lse = size_t(parts) * rows * sizeof(float);
-    return (o + 255) / 256 * 256 + (lse + 255) / 256 * 256;
-}
 
 hipError_t launch_fwd_split_bf16(SplitParams p, int d, int causal, hipStream_t stream) {
     if (p.scale_log2 > 0.f) {

@@ -89,6 +89,7 @@ E = _lib.STATUS_CODE
     (dict(causal=2), "FA_ERR_ARG"),
     (dict(scale=float("nan")), "FA_ERR_ARG"),
     (dict(scale=float("inf")), "FA_ERR_ARG"),
+    (dict(scale=3.0e38), "FA_ERR_ARG"),  # finite, but scale * log2(e) overflows float
 ])
 def test_fwd_rejects(kw, code):
     assert fwd(**kw) == E[code]
