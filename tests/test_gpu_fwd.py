@@ -151,3 +151,65 @@ def test_fwd_bad_shape_raises():
     k = torch.zeros((1, 2, 16, 64), device="cuda", dtype=torch.bfloat16)
     with pytest.raises(FAError):
         fwd(q, k, k.clone())
+
+
+# Launches with more (query block, head) items than compute units and short
+# items (causal N up to about 3.8K, non-causal up to 2K, windows) run
+# persistent: one workgroup per compute unit takes several items in a row.
+# Every item's arithmetic is the same whichever workgroup runs it, so a head
+# of such a launch equals, bit for bit, the same head computed in a launch
+# of one item per workgroup (a few heads alone).
+STREAMED = [  # B, Hq, Hkv, N, d, causal: B * Hq * ceil(N / 256) > 256 items
+    (1, 96, 96, 1000, 128, True),
+    (2, 64, 16, 700, 128, True),
+    (1, 160, 40, 520, 64, True),
+    (3, 48, 48, 600, 128, False),
+    (1, 192, 12, 300, 64, False),
+]
+
+
+@pytest.mark.parametrize("shape", STREAMED, ids=lambda s: "B{}Hq{}Hkv{}N{}d{}{}".format(*s[:5], "c" if s[5] else "n"))
+def test_fwd_streamed_launch(shape):
+    require_gpu()
+    B, Hq, Hkv, N, d, causal = shape
+    G = Hq // Hkv
+    q, k, v = (t.cuda() for t in inputs.make(B, Hq, Hkv, N, d, torch.bfloat16, 900 + N + d))
+    o, lse = fwd(q, k, v, causal=causal)
+    # the first and last key/value head's query heads, alone (one item per workgroup)
+    for b, g in ((0, 0), (B - 1, Hkv - 1)):
+        hs = slice(g * G, (g + 1) * G)
+        o1, l1 = fwd(q[b:b + 1, hs].contiguous(), k[b:b + 1, g:g + 1].contiguous(), v[b:b + 1, g:g + 1].contiguous(),
+                     causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], o[b, hs]) and torch.equal(l1[0], lse[b, hs]), (b, g)
+    # and the oracle on two heads
+    for b, h in ((0, 0), (B - 1, Hq - 1)):
+        g = h // G
+        O, LSE = oracle.head_forward(f64(q[b, h]), f64(k[b, g]), f64(v[b, g]), d ** -0.5, causal)
+        assert maxabs(f64(o[b, h]), O) <= TOL[torch.bfloat16]["out"]
+        assert maxabs(lse[b, h].cpu().numpy(), LSE) <= TOL[torch.bfloat16]["lse"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_streamed_window_and_dropout(d):
+    """The window and dropout kernels take the persistent launch as well."""
+    require_gpu()
+    from io_aware_transformer_amd import fwd_dropout, fwd_window
+
+    B, H, N = 2, 96, 900
+    q, k, v = (t.cuda() for t in inputs.make(B, H, H, N, d, torch.bfloat16, 950 + d))
+    ow, lw = fwd_window(q, k, v, (300, 0))
+    od, ld = fwd_dropout(q, k, v, 0.2, 77, 3)
+    hs = slice(H - 3, H)
+    ow1, lw1 = fwd_window(q[1:, hs].contiguous(), k[1:, hs].contiguous(), v[1:, hs].contiguous(), (300, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(ow1[0], ow[1, hs]) and torch.equal(lw1[0], lw[1, hs])
+    # dropout: the keep mask depends on (b, h) of the full batch, so compare with the oracle
+    h = H - 1
+    O, LSE = oracle.dropout_head_forward(f64(q[1, h]), f64(k[1, h]), f64(v[1, h]), d ** -0.5, True, 0.2, 77, 3,
+                                         1 * H + h)
+    assert maxabs(f64(od[1, h]), O) <= TOL[torch.bfloat16]["out"]
+    assert maxabs(ld[1, h].cpu().numpy(), LSE) <= TOL[torch.bfloat16]["lse"]
+    Ow, LSEw = oracle.window_forward(f64(q[:1, 5:6]), f64(k[:1, 5:6]), f64(v[:1, 5:6]), d ** -0.5, 300, 0)
+    assert maxabs(f64(ow[:1, 5:6]), Ow) <= TOL[torch.bfloat16]["out"]
+    assert maxabs(lw[:1, 5:6].cpu().numpy(), LSEw) <= TOL[torch.bfloat16]["lse"]

@@ -86,8 +86,8 @@ def test_varlen_bwd(mix, heads, causal, d):
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_equal_lengths_match_fixed_entry(causal, d):
     """B sequences of one length run the same kernels as fa_fwd / fa_bwd on
-    the [B, H, N, d] batch: results are bit-identical after the layout
-    change."""
+    the [B, H, N, d] batch: O, LSE and dQ are bit-identical after the layout
+    change (dK / dV up to the summation order of grouped heads)."""
     require_gpu()
     B, Hq, Hkv, N = 3, 4, 2, 333
     q, k, v, do = inputs.make(B, Hq, Hkv, N, d, BF, 17, with_grad=True)
@@ -107,8 +107,14 @@ def test_varlen_equal_lengths_match_fixed_entry(causal, d):
     torch.cuda.synchronize()
     assert torch.equal(unpack(po), o)
     assert torch.equal(plse.reshape(Hq, B, N).permute(1, 0, 2), lse)
-    for x, y in zip(pg, g):
-        assert torch.equal(unpack(x), y)
+    assert torch.equal(unpack(pg[0]), g[0])
+    for x, y in zip(pg[1:], g[1:]):
+        # fa_bwd splits each key/value head's query heads over workgroups
+        # and sums their float partials; the packed backward sums the group
+        # in one workgroup: both round one float sum to bf16, at most one
+        # bf16 ulp apart.
+        x, y = unpack(x).float(), y.float()
+        assert torch.all((x - y).abs() <= 2.0 ** -7 * torch.maximum(x.abs(), y.abs()) + 1e-6)
 
 
 def test_varlen_max_seqlen_above_longest():
