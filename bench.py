@@ -253,6 +253,11 @@ def bench_split(args, p):
         for _ in range(warmup):
             fwd_split(q, k, v, scale=p.scale, causal=p.causal, num_splits=splits, out=o, lse=lse, workspace=ws)
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.min_warmup_seconds:
+            for _ in range(20):
+                fwd_split(q, k, v, scale=p.scale, causal=p.causal, num_splits=splits, out=o, lse=lse, workspace=ws)
+            torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for e in evs:
             e[0].record(stream)
@@ -357,6 +362,12 @@ def bench_varlen(args, p):
             f()
             b()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.min_warmup_seconds:
+            for _ in range(5):
+                f()
+                b()
+            torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         for e in evs:
             e[0].record(stream)
@@ -458,6 +469,9 @@ def main():
     ap.add_argument("--dropout", default=None, help="P: dropout probability on P through fa_fwd_dropout / "
                                                     "fa_bwd_dropout (FLOP counted as without dropout)")
     ap.add_argument("--no-legs", action="store_true", help="do not add the N=8192 leg to the default run")
+    ap.add_argument("--min-warmup-seconds", type=float, default=0.5,
+                    help="after the --warmup steps, keep warming up (untimed) until this much time has passed, so "
+                         "the timed steps run at the settled shader clock (0: exactly --warmup steps)")
     args = ap.parse_args()
 
     if args.print_source_hash:
@@ -647,6 +661,13 @@ def measure_fixed(args, p, passes, mode, dev, steps=None, warmup=None, cold_reps
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # The shader clock settles only after some time under load: the warm-up
+    # goes on, untimed, until it has lasted --min-warmup-seconds.
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.min_warmup_seconds:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
