@@ -106,22 +106,24 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------- bwd_dkdv v2
-// One workgroup of 4 waves per (batch, kv head, block of 32*KPW*4 keys); each
-// wave keeps KPW blocks of 32 keys (K and V rows as MFMA B operands) and
-// their dK, dV accumulators.  Query tiles of 64 rows (Q, dO in padded K
+// One workgroup of NW waves per (batch, kv head, block of 32*KPW*NW keys);
+// each wave keeps KPW blocks of 32 keys (K and V rows as MFMA B operands)
+// and their dK, dV accumulators.  Query tiles of 64 rows (Q, dO in padded K
 // slabs, LSE and D) are copied global -> LDS by buffer loads, 3-stage, two
-// tiles ahead.  With KPW = 2 every Q / dO fragment read from LDS feeds two
-// products (LDS traffic per FLOP halves); the accumulators are touched by
-// the matrix cores only until the epilogue.
+// tiles ahead.  KPW = 2 would let every Q / dO fragment read from LDS feed
+// two products; at d = 64, 8 waves of one block each (two per SIMD, one
+// wave's exponentials and dS under the other's matrix products) measured
+// 7-10 % faster.  The accumulators are touched by the matrix cores only
+// until the epilogue.
 template <int D>
 struct DkCfg;
 template <>
 struct DkCfg<64> {
-    static constexpr int KPW = 2;
+    static constexpr int KPW = 1, NW = 8;
 };
 template <>
 struct DkCfg<128> {
-    static constexpr int KPW = 1;
+    static constexpr int KPW = 1, NW = 4;
 };
 constexpr int kDkWaves = 4;
 constexpr int kDkBQ = 64;
@@ -138,11 +140,11 @@ struct DkLds {
 
 template <int D>
 constexpr int dk_keys_per_wg() {
-    return 32 * DkCfg<D>::KPW * kDkWaves;
+    return 32 * DkCfg<D>::KPW * DkCfg<D>::NW;
 }
 
 template <int D, int MASK, bool DROP>
-__global__ __launch_bounds__(kDkWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(DkCfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(DkCfg<D>::NW / 4, DkCfg<D>::NW / 4)))
 void bwd_dkdv2_kernel(BwdParams p) {
     // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
     // time); 2: the window (p.wl, p.wr).
@@ -156,8 +158,9 @@ void bwd_dkdv2_kernel(BwdParams p) {
     constexpr int SB = DkLds<D>::STAGE_BYTES;
     constexpr int NST = kDkStages;
     constexpr int BQ = kDkBQ;
-    constexpr int PPW = QL::PIECES / kDkWaves;  // copy pieces per wave per matrix
-    static_assert(QL::PIECES % kDkWaves == 0, "pieces must split over the waves");
+    constexpr int NW = DkCfg<D>::NW;
+    constexpr int PPW = QL::PIECES / NW;  // copy pieces per wave per matrix
+    static_assert(QL::PIECES % NW == 0, "pieces must split over the waves");
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
 
     const int tid = threadIdx.x;
@@ -219,7 +222,7 @@ void bwd_dkdv2_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
         int r, e0;
-        QL::piece_src(w + kDkWaves * i, lane, r, e0);
+        QL::piece_src(w + NW * i, lane, r, e0);
         src_off[i] = r * D + e0;
     }
     auto issue = [&](int t) {
@@ -233,7 +236,7 @@ void bwd_dkdv2_kernel(BwdParams p) {
         const bool tail = q0 + BQ > N;
 #pragma unroll
         for (int i = 0; i < PPW; ++i) {
-            const int pi = w + kDkWaves * i;
+            const int pi = w + NW * i;
             uint32_t off = uint32_t(src_off[i]);
             if (tail) off = uint32_t(min(src_off[i] / D, N - 1 - q0) * D + src_off[i] % D);
             buf16_to_lds(qr, 2 * off, st + 2 * QL::piece_dst(pi));
@@ -778,13 +781,17 @@ void bwd_dkdv3_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- bwd_dq v2
-// One workgroup of 4 waves per (batch, query head, 256 queries); each wave
-// owns two 32-row blocks (Q and dO rows as B operands, dQ accumulators), so
-// every K / V fragment read from LDS feeds two products.  K/V tiles of 64
+// One workgroup of 8 waves per (batch, query head, 256 queries); each wave
+// owns kDqRB 32-row blocks (Q and dO rows as B operands, dQ accumulators).
+// With one block per wave (about 230 registers at d = 128) two waves share
+// each SIMD, and one wave's softmax and dS arithmetic runs while the other's
+// matrix products do (4 waves of two blocks each, which read every K / V
+// fragment once for two products, measured 2-7 % slower).  K/V tiles of 64
 // keys (padded K slabs: row reads for S^T = K Q^T, transposing reads for
 // dQ^T += K^T dS^T) are copied global -> LDS by buffer loads, 3-stage.
-constexpr int kDqWaves = 4;
-constexpr int kDqBM = 64 * kDqWaves;
+constexpr int kDqRB = 1;  // 32-row blocks per wave
+constexpr int kDqWaves = 8 / kDqRB;
+constexpr int kDqBM = 256;
 constexpr int kDqBN = 64;
 constexpr int kDqStages = 3;
 
@@ -797,7 +804,7 @@ struct DqLds {
 };
 
 template <int D, int MASK, bool DROP>
-__global__ __launch_bounds__(kDqWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kDqWaves * 64) __attribute__((amdgpu_waves_per_eu(kDqWaves / 4, kDqWaves / 4)))
 void bwd_dq2_kernel(BwdParams p) {
     // MASK 0: no mask; 1: causal (window (unbounded, 0), folded at compile
     // time); 2: the window (p.wl, p.wr).
@@ -836,15 +843,16 @@ void bwd_dq2_kernel(BwdParams p) {
     const bf16* __restrict__ Vh = static_cast<const bf16*>(p.V) + kvoff;
 
     const int q0 = qb * kDqBM;
-    const int wq0 = q0 + 64 * w;
-    const int wq_last = wq0 + 63;
+    constexpr int RB = kDqRB;
+    const int wq0 = q0 + 32 * RB * w;
+    const int wq_last = wq0 + 32 * RB - 1;
 
-    bf16x8 qreg[2][D / 16], oreg[2][D / 16];
-    float lse2[2], drow[2];
-    int key_lim[2], key_lo[2];  // visible keys of each row block's lane: key_lo .. key_lim
-    f32x16 acc[2][D / 32];
+    bf16x8 qreg[RB][D / 16], oreg[RB][D / 16];
+    float lse2[RB], drow[RB];
+    int key_lim[RB], key_lo[RB];  // visible keys of each row block's lane: key_lo .. key_lim
+    f32x16 acc[RB][D / 32];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const int qrow = wq0 + 32 * rb + l32;
 #pragma unroll
         for (int cc = 0; cc < D / 16; ++cc) {
@@ -891,7 +899,7 @@ void bwd_dq2_kernel(BwdParams p) {
         else return (kt0 + kt) * BN;
     };
     auto wave_sees = [&](int kt) -> bool {
-        if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane(lds_i32(tlist + kt)) >> (24 + (w >> 1))) & 1;
+        if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane(lds_i32(tlist + kt)) >> (24 + (wq0 - q0) / 128)) & 1;
         else return true;
     };
 
@@ -940,21 +948,22 @@ void bwd_dq2_kernel(BwdParams p) {
             if (!sees || (CAUSAL && (kb0 > wq_last + wr_ || (WIN && kb0 + 31 < wq0 - wl_))) || kb0 >= N) continue;
             // S^T = K Q^T, dP^T = V dO^T for both row blocks: lane = query,
             // register r = key kb0 + 8(r/4) + 4hi + r%4
-            f32x16 s[2], dpt[2];
-            s[0] = s[1] = dpt[0] = dpt[1] = f32x16{};
+            f32x16 s[RB], dpt[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) s[rb] = dpt[rb] = f32x16{};
 #pragma unroll
             for (int cc = 0; cc < D / 16; ++cc) {
                 const bf16x8 ak = as_bf16x8(lds16(Ks + KL::off(32 * kb + l32, 16 * cc + 8 * hi)));
                 const bf16x8 av = as_bf16x8(lds16(Vs + KL::off(32 * kb + l32, 16 * cc + 8 * hi)));
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
+                for (int rb = 0; rb < RB; ++rb) {
                     s[rb] = mfma_32x32x16(ak, qreg[rb][cc], s[rb]);
                     dpt[rb] = mfma_32x32x16(av, oreg[rb][cc], dpt[rb]);
                 }
             }
-            bf16x8 sb[2][2];
+            bf16x8 sb[RB][2];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) {
                 float ds[16];
                 uint32_t dy[4];  // dropout keep bytes: dP is dropped and scaled before dS
                 if constexpr (DROP)
@@ -994,8 +1003,8 @@ void bwd_dq2_kernel(BwdParams p) {
                 for (int db = 0; db < D / 32; ++db) {
                     const bf16x8 a = cat(lds_read_tr(Ks + KL::off(kr, db * 32 + tcol)),
                                          lds_read_tr(Ks + KL::off(kr + 8, db * 32 + tcol)));
-                    acc[0][db] = mfma_32x32x16(a, sb[0][cc], acc[0][db]);
-                    acc[1][db] = mfma_32x32x16(a, sb[1][cc], acc[1][db]);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) acc[rb][db] = mfma_32x32x16(a, sb[rb][cc], acc[rb][db]);
                 }
             }
         }
@@ -1007,7 +1016,7 @@ void bwd_dq2_kernel(BwdParams p) {
     }
 
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const int qrow = wq0 + 32 * rb + l32;
         if (qrow < N) {
             bf16* dQr = static_cast<bf16*>(p.dQ) + qrows * D + size_t(qrow) * D;
@@ -1054,7 +1063,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
         if ((e = set_max_dynamic_lds(kern, lds, attr)) != hipSuccess) return e;
         p.nkb = (p.N + dk_keys_per_wg<D>() - 1) / dk_keys_per_wg<D>();
         const long long blocks = (long long)p.nkb * p.B * p.Hkv * p.hsplit;
-        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kDkWaves * 64), lds, stream, p);
+        hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(DkCfg<D>::NW * 64), lds, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 2b. sum of the query-head slices' partials
