@@ -519,7 +519,7 @@ def main():
         line["legs"] = {"c3a": leg_summary(inputs.PRESETS["c3a"], m3)}
     line["clock"] = m["clock"]
     if args.cpu_seconds > 0 and mode.kind == "dense":
-        line["cpu_baseline"] = cpu_baseline(p, passes, args.cpu_seconds, m)
+        line["cpu_baseline"] = cpu_baseline(p, m["passes"], args.cpu_seconds, m)
     print(json.dumps(line), flush=True)
 
 
