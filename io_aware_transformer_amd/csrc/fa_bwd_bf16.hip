@@ -658,12 +658,12 @@ void bwd_dkdv3_kernel(BwdParams p) {
         const int thr = CAUSAL ? kw0 + l32 - wr_ - qb0 - 4 * hi : -1 - 4 * hi;     // q < key - wr
         const int thr_hi = WIN ? kw0 + l32 + wl_ - qb0 - 4 * hi : kUnbounded;  // q > key + wl
         const int nlim = N - qb0 - 4 * hi;                                          // q >= N
-        if (has_next) s_nxt = dp_nxt = f32x16{};
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
             if (has_next) {
-                s_nxt = mfma_32x32x16(aq[k], kreg[k], s_nxt);
-                dp_nxt = mfma_32x32x16(ao[k], vreg[k], dp_nxt);
+                // the first product starts from an immediate zero (no register clearing)
+                s_nxt = mfma_32x32x16(aq[k], kreg[k], k == 0 ? f32x16{} : s_nxt);
+                dp_nxt = mfma_32x32x16(ao[k], vreg[k], k == 0 ? f32x16{} : dp_nxt);
             }
 #pragma unroll
             for (int n = k * TPC; n < (k + 1) * TPC; ++n) load_tr(i, n);

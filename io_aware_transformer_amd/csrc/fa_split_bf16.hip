@@ -28,6 +28,8 @@
 //
 // lse_merge_kernel<D, OutT>: one group of D/4 lanes per row, four dims per
 // lane; reads every part's LSE, then accumulates the weighted parts.
+// lse_merge_wide_kernel<D, OutT>: the same per group of parts, one
+// workgroup per row, for many parts over few rows.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -299,6 +301,64 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* _
     if (t == 0 && LSE != nullptr) LSE[row] = tot > 0.f ? M + logf(tot) : -INFINITY;
 }
 
+// Many parts (decoding steps split over many key ranges, few rows): one
+// workgroup of 256 threads per row; the row's parts are dealt to 256 / (D/4)
+// lane groups, each group merges its own parts as above (its own max, sum
+// and weighted output), and the groups' partials are merged through LDS
+// with the same rule: M = max_g M_g, sum = sum_g sum_g e^{M_g - M},
+// O = sum_g acc_g e^{M_g - M} / sum.
+constexpr int kMergeWideThreads = 256;
+template <int D, typename OutT>
+__global__ __launch_bounds__(kMergeWideThreads) void lse_merge_wide_kernel(const float* __restrict__ Op,
+                                                                           const float* __restrict__ Lp, int parts,
+                                                                           long long rows, OutT* __restrict__ O,
+                                                                           float* __restrict__ LSE) {
+    constexpr int TPR = D / 4;                     // lanes per part group, four dims each
+    constexpr int PG = kMergeWideThreads / TPR;    // part groups
+    __shared__ float sm[PG], ssum[PG];
+    __shared__ f32x4 sacc[PG][TPR];
+    const long long row = blockIdx.x;
+    const int t = threadIdx.x % TPR, g = threadIdx.x / TPR;
+    float m = -INFINITY;
+    for (int q = g; q < parts; q += PG) m = fmaxf(m, Lp[(long long)q * rows + row]);
+    float tot = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (m != -INFINITY) {
+        for (int q = g; q < parts; q += PG) {
+            const float lq = Lp[(long long)q * rows + row];
+            const f32x4 v = *reinterpret_cast<const f32x4*>(Op + ((long long)q * rows + row) * D + 4 * t);
+            const float wq = lq == -INFINITY ? 0.f : expf(lq - m);  // empty parts hold O_p = 0
+            tot += wq;
+            acc += wq * v;
+        }
+    }
+    if (t == 0) {
+        sm[g] = m;
+        ssum[g] = tot;
+    }
+    sacc[g][t] = acc;
+    __syncthreads();
+    if (g != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < PG; ++k) M = fmaxf(M, sm[k]);
+    float sum = 0.f;
+    f32x4 out = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < PG; ++k) {
+            const float f = sm[k] == -INFINITY ? 0.f : expf(sm[k] - M);
+            sum += ssum[k] * f;
+            out += f * sacc[k][t];
+        }
+    }
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    OutT* orow = O + row * D + 4 * t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[e] = OutT(out[e] * inv);
+    if (t == 0 && LSE != nullptr) LSE[row] = sum > 0.f ? M + logf(sum) : -INFINITY;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_split_t(SplitParams p, hipStream_t stream) {
     auto kern = fwd_split_kernel<D, CAUSAL>;
@@ -316,6 +376,13 @@ template <int D, typename OutT>
 hipError_t launch_merge_t(const float* Op, const float* Lp, int parts, long long rows, void* O, float* LSE,
                           hipStream_t stream) {
     constexpr int TPR = D / 4;
+    if (parts >= 8 && rows <= (1LL << 16)) {
+        // many parts over few rows: one workgroup per row (the narrow kernel would
+        // leave each lane a long chain of dependent loads)
+        hipLaunchKernelGGL((lse_merge_wide_kernel<D, OutT>), dim3(unsigned(rows)), dim3(kMergeWideThreads), 0,
+                           stream, Op, Lp, parts, rows, static_cast<OutT*>(O), LSE);
+        return hipGetLastError();
+    }
     constexpr int RPB = kMergeThreads / TPR > 0 ? kMergeThreads / TPR : 1;
     constexpr int THREADS = RPB * TPR;  // 64, or one row of 64 lanes at d = 256
     const long long blocks = (rows + RPB - 1) / RPB;

@@ -106,7 +106,7 @@ def test_split_presets_full(name):
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("parts,rows", [(1, 1), (2, 5), (7, 300)])
+@pytest.mark.parametrize("parts,rows", [(1, 1), (2, 5), (7, 300), (8, 4), (37, 300), (128, 40)])
 @pytest.mark.parametrize("dtype", [torch.float32, BF], ids=["fp32", "bf16"])
 def test_merge(d, parts, rows, dtype):
     require_gpu()
