@@ -213,3 +213,30 @@ def test_fwd_streamed_window_and_dropout(d):
     Ow, LSEw = oracle.window_forward(f64(q[:1, 5:6]), f64(k[:1, 5:6]), f64(v[:1, 5:6]), d ** -0.5, 300, 0)
     assert maxabs(f64(ow[:1, 5:6]), Ow) <= TOL[torch.bfloat16]["out"]
     assert maxabs(lw[:1, 5:6].cpu().numpy(), LSEw) <= TOL[torch.bfloat16]["lse"]
+
+
+def test_fwd_streamed_launch_beyond_item_table():
+    """More (query block, head) items than 512 per compute unit: the launch
+    grows its grid past one workgroup per compute unit so that no workgroup
+    holds more items than its LDS table (B3 H65535 N256 d64 causal: 196605
+    items).  Heads of that launch equal, bit for bit, the same heads in
+    launches of one item per workgroup.  Inputs are drawn on the device
+    (26 GB of Q, K, V and O)."""
+    require_gpu()
+    B, H, N, d = 3, 65535, 256, 64
+    g = torch.Generator(device="cuda").manual_seed(4242)
+    q = torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    o, lse = fwd(q, k, v, causal=True)
+    for b, h in ((0, 0), (1, 31337), (2, H - 4)):
+        hs = slice(h, h + 4)
+        o1, l1 = fwd(q[b:b + 1, hs].contiguous(), k[b:b + 1, hs].contiguous(), v[b:b + 1, hs].contiguous(),
+                     causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], o[b, hs]) and torch.equal(l1[0], lse[b, hs]), (b, h)
+    O, LSE = oracle.head_forward(f64(q[2, H - 1]), f64(k[2, H - 1]), f64(v[2, H - 1]), d ** -0.5, True)
+    assert maxabs(f64(o[2, H - 1]), O) <= TOL[torch.bfloat16]["out"]
+    assert maxabs(lse[2, H - 1].cpu().numpy(), LSE) <= TOL[torch.bfloat16]["lse"]
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
