@@ -360,8 +360,9 @@ void bwd_dkdv2_kernel(BwdParams p) {
                                            ds[8 * cc + 5], ds[8 * cc + 6], ds[8 * cc + 7]);
                 }
             }
-            // dV += P^T dO, dK += dS^T Q: dO and Q enter as B operands through
-            // transposing reads, each fragment feeding KPW products.
+            // dV^T += dO^T P, dK^T += Q^T dS: dO and Q enter as A operands
+            // through transposing reads, each fragment feeding KPW products
+            // (the transposed products leave one key per lane).
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int qr = 32 * qs + 16 * cc + trow;
@@ -373,8 +374,8 @@ void bwd_dkdv2_kernel(BwdParams p) {
                                           lds_read_tr(Qs + QL::off(qr + 8, db * 32 + tcol)));
 #pragma unroll
                     for (int kb = 0; kb < KPW; ++kb) {
-                        dv[kb][db] = mfma_32x32x16(pb[kb][cc], bo, dv[kb][db]);
-                        dk[kb][db] = mfma_32x32x16(sb[kb][cc], bq, dk[kb][db]);
+                        dv[kb][db] = mfma_32x32x16(bo, pb[kb][cc], dv[kb][db]);
+                        dk[kb][db] = mfma_32x32x16(bq, sb[kb][cc], dk[kb][db]);
                     }
                 }
             }
@@ -388,29 +389,39 @@ void bwd_dkdv2_kernel(BwdParams p) {
         barrier_lds();
     }
 
-    // Epilogue: lane holds dim db*32 + l32 of keys kw0 + 32kb + 8(r/4) + 4hi + r%4.
-    bf16* dKh = static_cast<bf16*>(p.dK) + kvoff;
-    bf16* dVh = static_cast<bf16*>(p.dV) + kvoff;
+    // Epilogue: lane holds key kw0 + 32kb + l32, dims db*32 + 8(r/4) + 4hi + r%4;
+    // whole rows through this wave's LDS region.
+    const float vscale = DROP ? 256.f / float(256 - p.drop_t8) : 1.f;
+    __syncthreads();
 #pragma unroll
     for (int kb = 0; kb < KPW; ++kb) {
+        const int k0 = kw0 + 32 * kb;
+        const size_t row0 = kvoff + size_t(k0) * D;
+        if (S == 1) {
+            static_assert(NW * staged_rows_bytes<D, bf16>() <= int(DkLds<D>::BYTES), "staging must fit");
+            unsigned char* stg = smem_raw + w * staged_rows_bytes<D, bf16>();
+            store_rows_staged<D>(stg, dk[kb], p.scale, static_cast<bf16*>(p.dK) + row0, N - k0, lane);
+            store_rows_staged<D>(stg, dv[kb], vscale, static_cast<bf16*>(p.dV) + row0, N - k0, lane);
+        } else if constexpr (NW * staged_rows_bytes<D, float>() <= int(DkLds<D>::BYTES)) {
+            unsigned char* stg = smem_raw + w * staged_rows_bytes<D, float>();
+            store_rows_staged<D>(stg, dk[kb], p.scale, p.dk_part + sl * p.part_stride + row0, N - k0, lane);
+            store_rows_staged<D>(stg, dv[kb], vscale, p.dv_part + sl * p.part_stride + row0, N - k0, lane);
+        } else if (k0 + l32 < N) {
+            // float partials without room to stage: four consecutive dims per store
+            float* dkr = p.dk_part + sl * p.part_stride + row0 + size_t(l32) * D;
+            float* dvr = p.dv_part + sl * p.part_stride + row0 + size_t(l32) * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kk = kw0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (kk < N) {
-                    const float kval = dk[kb][db][r] * p.scale;
-                    const float vval = DROP ? dv[kb][db][r] * (256.f / float(256 - p.drop_t8)) : dv[kb][db][r];
-                    const size_t e = size_t(kk) * D + db * 32 + l32;
-                    if (S == 1) {
-                        dKh[e] = (bf16)kval;
-                        dVh[e] = (bf16)vval;
-                    } else {
-                        p.dk_part[sl * p.part_stride + kvoff + e] = kval;
-                        p.dv_part[sl * p.part_stride + kvoff + e] = vval;
-                    }
+                for (int g = 0; g < 4; ++g) {
+                    const int e = db * 32 + 8 * g + 4 * hi;
+                    const f32x16& a = dk[kb][db];
+                    const f32x16& v = dv[kb][db];
+                    *reinterpret_cast<f32x4*>(dkr + e) = f32x4{a[4 * g] * p.scale, a[4 * g + 1] * p.scale,
+                                                               a[4 * g + 2] * p.scale, a[4 * g + 3] * p.scale};
+                    *reinterpret_cast<f32x4*>(dvr + e) = f32x4{v[4 * g] * vscale, v[4 * g + 1] * vscale,
+                                                               v[4 * g + 2] * vscale, v[4 * g + 3] * vscale};
                 }
-            }
         }
     }
 }
@@ -420,8 +431,9 @@ void bwd_dkdv2_kernel(BwdParams p) {
 // query subtiles of 32 rows (two per staged 64-row tile).  Subtile i passes
 // through three steps: A(i) S = Q K^T, dP = dO V^T (matrix cores, row reads
 // of Q / dO issued one step ahead); B(i) P = exp2(c S - LSE log2 e),
-// dS = P o (dP - D) (vector ALU); C(i) dV += P^T dO, dK += dS^T Q (matrix
-// cores, transposing reads of dO / Q).  The loop body for subtile i runs
+// dS = P o (dP - D) (vector ALU); C(i) dV^T += dO^T P, dK^T += Q^T dS
+// (matrix cores, transposing reads of dO / Q; the transposed products leave
+// one key per lane, so the epilogue stores whole rows).  The loop body for subtile i runs
 // A(i+1) together with B(i) and the transposing reads of C(i), then C(i)
 // together with the row reads for A(i+2): every LDS read has a whole step
 // of slack before its first use, and the LDS traffic is split evenly over
@@ -696,8 +708,8 @@ void bwd_dkdv3_kernel(BwdParams p) {
 #pragma unroll
         for (int m = 0; m < NC; ++m) {
             const int cc = m / NDB, db = m % NDB;
-            dv[db] = mfma_32x32x16(pb[cc], bo[cc][db], dv[db]);
-            dk[db] = mfma_32x32x16(sb[cc], bq[cc][db], dk[db]);
+            dv[db] = mfma_32x32x16(bo[cc][db], pb[cc], dv[db]);
+            dk[db] = mfma_32x32x16(bq[cc][db], sb[cc], dk[db]);
             if (has_next2) load_a(i + 2, m);
             if (has_next && m < 4) load_stats(i + 1, m);
             __builtin_amdgcn_sched_barrier(0);
@@ -759,24 +771,18 @@ void bwd_dkdv3_kernel(BwdParams p) {
     body(nsub - 1, s1, dp1, s0, dp0, false, false);
     wait_vmem();  // no copy into LDS may outlive the workgroup
 
-    bf16* dKh = static_cast<bf16*>(p.dK) + kvoff;
-    bf16* dVh = static_cast<bf16*>(p.dV) + kvoff;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kk = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (kk < N) {
-                const size_t e = size_t(kk) * D + db * 32 + l32;
-                if (S == 1) {
-                    dKh[e] = (bf16)(dk[db][r] * p.scale);
-                    dVh[e] = (bf16)(dv[db][r]);
-                } else {
-                    p.dk_part[sl * p.part_stride + kvoff + e] = dk[db][r] * p.scale;
-                    p.dv_part[sl * p.part_stride + kvoff + e] = dv[db][r];
-                }
-            }
-        }
+    // dK, dV (lane = key kw0 + l32, registers = dims): whole rows through
+    // this wave's LDS region once every wave is past its last read.
+    static_assert(kDkWaves * staged_rows_bytes<D, float>() <= int(Dk3Lds<D>::BYTES), "staging must fit");
+    __syncthreads();
+    unsigned char* stg = smem_raw + w * staged_rows_bytes<D, float>();
+    const size_t row0 = kvoff + size_t(kw0) * D;
+    if (S == 1) {
+        store_rows_staged<D>(stg, dk, p.scale, static_cast<bf16*>(p.dK) + row0, N - kw0, lane);
+        store_rows_staged<D>(stg, dv, 1.f, static_cast<bf16*>(p.dV) + row0, N - kw0, lane);
+    } else {
+        store_rows_staged<D>(stg, dk, p.scale, p.dk_part + sl * p.part_stride + row0, N - kw0, lane);
+        store_rows_staged<D>(stg, dv, 1.f, p.dv_part + sl * p.part_stride + row0, N - kw0, lane);
     }
 }
 
@@ -1015,22 +1021,15 @@ void bwd_dq2_kernel(BwdParams p) {
         barrier_lds();
     }
 
+    // dQ (lane = query row): whole rows through this wave's LDS region once
+    // every wave is past its last read.
+    static_assert(kDqWaves * staged_rows_bytes<D, bf16>() <= int(DqLds<D>::BYTES), "staging must fit");
+    __syncthreads();
+    unsigned char* stg = smem_raw + w * staged_rows_bytes<D, bf16>();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int qrow = wq0 + 32 * rb + l32;
-        if (qrow < N) {
-            bf16* dQr = static_cast<bf16*>(p.dQ) + qrows * D + size_t(qrow) * D;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bf16x4 v =
-                        bf16x4{(bf16)(acc[rb][db][4 * j + 0] * p.scale), (bf16)(acc[rb][db][4 * j + 1] * p.scale),
-                               (bf16)(acc[rb][db][4 * j + 2] * p.scale), (bf16)(acc[rb][db][4 * j + 3] * p.scale)};
-                    *reinterpret_cast<bf16x4*>(dQr + db * 32 + 8 * j + 4 * hi) = v;
-                }
-            }
-        }
+        const int r0 = wq0 + 32 * rb;
+        store_rows_staged<D>(stg, acc[rb], p.scale, static_cast<bf16*>(p.dQ) + qrows * D + size_t(r0) * D, N - r0, lane);
     }
 }
 

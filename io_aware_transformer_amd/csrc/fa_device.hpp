@@ -379,6 +379,47 @@ __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_s_barrier();
 }
 
+// Stores 32 rows of a row-major [rows, D] matrix that one wave holds in the
+// accumulator layout of 32x32x16 products with the row as the N index (lane
+// l: row l % 32; register r of block db: column 32 db + 8 (r / 4) +
+// 4 (l / 32) + r % 4), scaled by f and converted to T (bf16 or float).  The
+// rows pass through the wave's own LDS region `stg` (32 (D sizeof(T) + 16)
+// bytes, 16-byte aligned, free of every other wave's use) so that each
+// global store writes whole rows, 16 bytes per lane, rather than four
+// values per lane scattered over 64 rows.  Rows at or past `nrows` are
+// skipped.  LDS operations of one wave execute in order, so the region can
+// be reused for the next matrix straight away.
+template <int D, typename T>
+__device__ __forceinline__ void store_rows_staged(unsigned char* stg, const f32x16 (&acc)[D / 32], float f, T* dst,
+                                                  int nrows, int lane) {
+    constexpr int ES = int(sizeof(T));
+    constexpr int ROWB = D * ES + 16;
+    const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            unsigned char* a = stg + l32 * ROWB + (db * 32 + 8 * g + 4 * hi) * ES;
+            const float x0 = acc[db][4 * g] * f, x1 = acc[db][4 * g + 1] * f;
+            const float x2 = acc[db][4 * g + 2] * f, x3 = acc[db][4 * g + 3] * f;
+            if constexpr (ES == 2) *reinterpret_cast<bf16x4*>(a) = bf16x4{(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
+            else *reinterpret_cast<f32x4*>(a) = f32x4{x0, x1, x2, x3};
+        }
+    constexpr int LPR = D * ES / 16;  // lanes per row
+    constexpr int RPI = 64 / LPR;     // rows per read
+    static_assert(LPR * RPI == 64 && 32 % RPI == 0, "rows must tile the wave");
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = it * RPI + lane / LPR, c = lane % LPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * ROWB + c * 16);
+        if (row < nrows) *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst + size_t(row) * D) + c * 16) = v;
+    }
+}
+template <int D, typename T>
+constexpr int staged_rows_bytes() {
+    return 32 * (D * int(sizeof(T)) + 16);
+}
+
 // Element offset of (row r, element e) in a row-read tile.
 template <int D>
 __device__ __forceinline__ int off_row(int r, int e) {
