@@ -387,11 +387,13 @@ __device__ __forceinline__ void barrier_lds() {
 // bytes, 16-byte aligned, free of every other wave's use) so that each
 // global store writes whole rows, 16 bytes per lane, rather than four
 // values per lane scattered over 64 rows.  Rows at or past `nrows` are
-// skipped.  LDS operations of one wave execute in order, so the region can
-// be reused for the next matrix straight away.
-template <int D, typename T>
-__device__ __forceinline__ void store_rows_staged(unsigned char* stg, const f32x16 (&acc)[D / 32], float f, T* dst,
-                                                  int nrows, int lane) {
+// skipped; LD is the row stride of dst in elements (D, or more when the
+// call stores a column slice of wider rows).  LDS operations of one wave
+// execute in order, so the region can be reused for the next matrix (or
+// slice) straight away.
+template <int D, typename T, int LD = D>
+__device__ __forceinline__ void store_rows_staged(unsigned char* stg, const f32x16* acc, float f, T* dst, int nrows,
+                                                  int lane) {
     constexpr int ES = int(sizeof(T));
     constexpr int ROWB = D * ES + 16;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -412,7 +414,7 @@ __device__ __forceinline__ void store_rows_staged(unsigned char* stg, const f32x
     for (int it = 0; it < 32 / RPI; ++it) {
         const int row = it * RPI + lane / LPR, c = lane % LPR;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * ROWB + c * 16);
-        if (row < nrows) *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst + size_t(row) * D) + c * 16) = v;
+        if (row < nrows) *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst + size_t(row) * LD) + c * 16) = v;
     }
 }
 template <int D, typename T>

@@ -495,26 +495,56 @@ void fwd_pp_kernel(FwdParams p) {
 
     // Output of the finished item: O = o / l (bf16), LSE = m + log2 l
     // (natural log); then the accumulators start over.
-    auto epilogue = [&]() {
+    // O rows leave the wave in one of two ways.  At the end of a launch of
+    // one item per workgroup the stages are free: every wave stages its 32
+    // rows in LDS and stores whole rows, 16 bytes per lane.  Between items of
+    // a persistent launch (the stages busy), the two halves of the wave trade
+    // 8-byte chunks so that each lane stores 16 contiguous bytes of its row.
+    auto epilogue = [&](auto staged) {
         const float lt = half_swap_sum(l);
         // A row that sees no key at all (block-sparse only) has l = 0: O = 0,
         // LSE = -inf.  Dropout scales the kept terms by 256 / (256 - t8).
         float inv = (!SPARSE || lt > 0.f) ? 1.f / lt : 0.f;
         if constexpr (DROP) inv *= 256.f / float(256 - p.drop_t8);
-        if (qrow < cur.n) {
+        if constexpr (decltype(staged)::value) {
+            static_assert(kPPWaves * staged_rows_bytes<D, bf16>() <= int(pp_lds_bytes<D>()), "staging must fit");
+            store_rows_staged<D>(smem_raw + w * staged_rows_bytes<D, bf16>(), o, inv,
+                                 static_cast<bf16*>(p.O) + (cur.qrow0 + size_t(wq0)) * D, cur.n - wq0, lane);
+        } else if (qrow < cur.n) {
             bf16* orow = static_cast<bf16*>(p.O) + (cur.qrow0 + size_t(qrow)) * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const bf16x4 v = bf16x4{(bf16)(o[db][4 * jj + 0] * inv), (bf16)(o[db][4 * jj + 1] * inv),
+                for (int jj = 0; jj < 4; jj += 2) {
+                    if constexpr (D == 64) {  // measured: the trade does not pay for 128-byte rows
+                        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * jj + 4 * hi) =
+                            bf16x4{(bf16)(o[db][4 * jj + 0] * inv), (bf16)(o[db][4 * jj + 1] * inv),
+                                   (bf16)(o[db][4 * jj + 2] * inv), (bf16)(o[db][4 * jj + 3] * inv)};
+                        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * jj + 8 + 4 * hi) =
+                            bf16x4{(bf16)(o[db][4 * jj + 4] * inv), (bf16)(o[db][4 * jj + 5] * inv),
+                                   (bf16)(o[db][4 * jj + 6] * inv), (bf16)(o[db][4 * jj + 7] * inv)};
+                        continue;
+                    }
+                    // half 0 ends with dims 8jj .. 8jj+7 of its row, half 1 with 8jj+8 .. 8jj+15
+                    const bf16x4 a = bf16x4{(bf16)(o[db][4 * jj + 0] * inv), (bf16)(o[db][4 * jj + 1] * inv),
                                             (bf16)(o[db][4 * jj + 2] * inv), (bf16)(o[db][4 * jj + 3] * inv)};
-                    *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * jj + 4 * hi) = v;
+                    const bf16x4 b = bf16x4{(bf16)(o[db][4 * jj + 4] * inv), (bf16)(o[db][4 * jj + 5] * inv),
+                                            (bf16)(o[db][4 * jj + 6] * inv), (bf16)(o[db][4 * jj + 7] * inv)};
+                    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+                    u32x2 y;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int x = int(hi ? ua[e] : ub[e]);
+                        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+                        y[e] = uint32_t(hi ? r[0] : r[1]);
+                    }
+                    const u32x4 v = hi ? u32x4{y[0], y[1], ub[0], ub[1]} : u32x4{ua[0], ua[1], y[0], y[1]};
+                    *reinterpret_cast<u32x4*>(orow + db * 32 + 8 * (jj + hi)) = v;
                 }
             }
-            if (hi == 0 && p.LSE != nullptr)
-                p.LSE[cur.qrow0 + qrow] = (!SPARSE || lt > 0.f) ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
         }
+        if (qrow < cur.n && hi == 0 && p.LSE != nullptr)
+            p.LSE[cur.qrow0 + qrow] = (!SPARSE || lt > 0.f) ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         m = -3.0e38f;
@@ -634,7 +664,7 @@ void fwd_pp_kernel(FwdParams p) {
         if constexpr (STREAM) {
             pv(g);
             if (g == cur_start + cur.T) {
-                epilogue();
+                epilogue(std::false_type{});
                 if (g < TT) switch_item(g, step);
             }
             prefetch_q(g);
@@ -727,7 +757,14 @@ void fwd_pp_kernel(FwdParams p) {
             }
         }
     }
-    if constexpr (!STREAM) epilogue();
+    if constexpr (!STREAM) {
+        // Both groups end on the same barrier, each wave having drained its
+        // LDS reads before it and every copy having landed before the last
+        // tile was published: the stages are free for staging rows.  (At
+        // d = 256 staging through LDS costs registers the kernel has not got.)
+        if constexpr (D <= 128) epilogue(std::true_type{});
+        else epilogue(std::false_type{});
+    }
 }
 
 // Persistent launch (fixed lengths, no block map, d <= 128) when a query
