@@ -109,8 +109,9 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
 // One workgroup of NW waves per (batch, kv head, block of 32*KPW*NW keys);
 // each wave keeps KPW blocks of 32 keys (K and V rows as MFMA B operands)
 // and their dK, dV accumulators.  Query tiles of 64 rows (Q, dO in padded K
-// slabs, LSE and D) are copied global -> LDS by buffer loads, 3-stage, two
-// tiles ahead.  KPW = 2 would let every Q / dO fragment read from LDS feed
+// slabs, LSE and D) are copied global -> LDS by buffer loads, four stages,
+// three tiles ahead (2-3 % faster than three stages at d = 64).  KPW = 2
+// would let every Q / dO fragment read from LDS feed
 // two products; at d = 64, 8 waves of one block each (two per SIMD, one
 // wave's exponentials and dS under the other's matrix products) measured
 // 7-10 % faster.  The accumulators are touched by the matrix cores only
@@ -127,7 +128,7 @@ struct DkCfg<128> {
 };
 constexpr int kDkWaves = 4;
 constexpr int kDkBQ = 64;
-constexpr int kDkStages = 3;
+constexpr int kDkStages = 4;
 
 template <int D>
 struct DkLds {
@@ -249,10 +250,18 @@ void bwd_dkdv2_kernel(BwdParams p) {
             buf16_to_lds(rr, uint32_t(16 * lane), st + 2 * TB + w * BQ * 4);
         }
     };
-    // s_waitcnt vmcnt: allow this wave's copies of the newest tile to stay in flight.
-    auto wait_older = [&]() {
-        if (w < 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW + 1) & 15) | (((2 * PPW + 1) >> 4) << 14));
-        else __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW) & 15) | (((2 * PPW) >> 4) << 14));
+    // s_waitcnt vmcnt: the `ahead` tiles issued after the next one stay in flight
+    // (this wave's copies per tile: 2 PPW, plus the statistics in waves 0 and 1).
+    auto wait_older = [&](int ahead) {
+        if (ahead >= 2) {
+            if (w < 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * PPW + 2) & 15) | (((4 * PPW + 2) >> 4) << 14));
+            else __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * PPW) & 15) | (((4 * PPW) >> 4) << 14));
+        } else if (ahead == 1) {
+            if (w < 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW + 1) & 15) | (((2 * PPW + 1) >> 4) << 14));
+            else __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW) & 15) | (((2 * PPW) >> 4) << 14));
+        } else {
+            wait_vmem();
+        }
     };
 
     const int trow = 4 * hi + ((lane & 15) >> 2);
@@ -260,12 +269,12 @@ void bwd_dkdv2_kernel(BwdParams p) {
 
     if (iters > 0) issue(0);
     if (iters > 1) issue(1);
+    if (iters > 2) issue(2);
     wait_vmem();
     __syncthreads();
 
     for (int t = 0; t < iters; ++t) {
-        const bool more = t + 2 < iters;
-        if (more) issue(t + 2);
+        if (t + 3 < iters) issue(t + 3);
         const unsigned char* st = smem_raw + (t % NST) * SB;
         const bf16* Qs = reinterpret_cast<const bf16*>(st);
         const bf16* dOs = reinterpret_cast<const bf16*>(st + TB);
@@ -384,8 +393,7 @@ void bwd_dkdv2_kernel(BwdParams p) {
         // tile's remain; drain this wave's LDS reads (the stage just read is
         // refilled next) and meet at a plain barrier: a __syncthreads()
         // fence would also wait for the copy of the newest tile.
-        if (more) wait_older();
-        else wait_vmem();
+        wait_older(min(iters - 1, t + 3) - (t + 1));
         barrier_lds();
     }
 
@@ -794,12 +802,13 @@ void bwd_dkdv3_kernel(BwdParams p) {
 // matrix products do (4 waves of two blocks each, which read every K / V
 // fragment once for two products, measured 2-7 % slower).  K/V tiles of 64
 // keys (padded K slabs: row reads for S^T = K Q^T, transposing reads for
-// dQ^T += K^T dS^T) are copied global -> LDS by buffer loads, 3-stage.
+// dQ^T += K^T dS^T) are copied global -> LDS by buffer loads, four stages
+// with three tiles in flight (three stages measured 1 % slower).
 constexpr int kDqRB = 1;  // 32-row blocks per wave
 constexpr int kDqWaves = 8 / kDqRB;
 constexpr int kDqBM = 256;
 constexpr int kDqBN = 64;
-constexpr int kDqStages = 3;
+constexpr int kDqStages = 4;
 
 template <int D>
 struct DqLds {
@@ -938,12 +947,12 @@ void bwd_dq2_kernel(BwdParams p) {
 
     if (ntiles > 0) issue(0);
     if (ntiles > 1) issue(1);
+    if (ntiles > 2) issue(2);
     wait_vmem();
     __syncthreads();
 
     for (int kt = 0; kt < ntiles; ++kt) {
-        const bool more = kt + 2 < ntiles;
-        if (more) issue(kt + 2);
+        if (kt + 3 < ntiles) issue(kt + 3);
         const bf16* Ks = reinterpret_cast<const bf16*>(smem_raw + (kt % NST) * SB);
         const bf16* Vs = reinterpret_cast<const bf16*>(smem_raw + (kt % NST) * SB + TB);
         const int kstart = tile_key0(kt);
@@ -1016,7 +1025,9 @@ void bwd_dq2_kernel(BwdParams p) {
         }
         // as in the dK/dV kernel: own copies of the next tile, LDS reads
         // drained, plain barrier (no fence waiting for the newest copy)
-        if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW) & 15) | (((2 * PPW) >> 4) << 14));
+        const int ahead = min(ntiles - 1, kt + 3) - (kt + 1);  // tiles issued after kt + 1
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * PPW) & 15) | (((4 * PPW) >> 4) << 14));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW) & 15) | (((2 * PPW) >> 4) << 14));
         else wait_vmem();
         barrier_lds();
     }
