@@ -410,26 +410,11 @@ void bwd_dkdv2_kernel(BwdParams p) {
             unsigned char* stg = smem_raw + w * staged_rows_bytes<D, bf16>();
             store_rows_staged<D>(stg, dk[kb], p.scale, static_cast<bf16*>(p.dK) + row0, N - k0, lane);
             store_rows_staged<D>(stg, dv[kb], vscale, static_cast<bf16*>(p.dV) + row0, N - k0, lane);
-        } else if constexpr (NW * staged_rows_bytes<D, float>() <= int(DkLds<D>::BYTES)) {
+        } else {
+            static_assert(NW * staged_rows_bytes<D, float>() <= int(DkLds<D>::BYTES), "staging must fit");
             unsigned char* stg = smem_raw + w * staged_rows_bytes<D, float>();
             store_rows_staged<D>(stg, dk[kb], p.scale, p.dk_part + sl * p.part_stride + row0, N - k0, lane);
             store_rows_staged<D>(stg, dv[kb], vscale, p.dv_part + sl * p.part_stride + row0, N - k0, lane);
-        } else if (k0 + l32 < N) {
-            // float partials without room to stage: four consecutive dims per store
-            float* dkr = p.dk_part + sl * p.part_stride + row0 + size_t(l32) * D;
-            float* dvr = p.dv_part + sl * p.part_stride + row0 + size_t(l32) * D;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int e = db * 32 + 8 * g + 4 * hi;
-                    const f32x16& a = dk[kb][db];
-                    const f32x16& v = dv[kb][db];
-                    *reinterpret_cast<f32x4*>(dkr + e) = f32x4{a[4 * g] * p.scale, a[4 * g + 1] * p.scale,
-                                                               a[4 * g + 2] * p.scale, a[4 * g + 3] * p.scale};
-                    *reinterpret_cast<f32x4*>(dvr + e) = f32x4{v[4 * g] * vscale, v[4 * g + 1] * vscale,
-                                                               v[4 * g + 2] * vscale, v[4 * g + 3] * vscale};
-                }
         }
     }
 }
