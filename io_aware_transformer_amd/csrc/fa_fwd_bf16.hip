@@ -660,7 +660,12 @@ void fwd_pp_kernel(FwdParams p) {
     // The M phase of tile g at `step`, with the step's copies.  An item
     // ends after the PV of its last tile (g - 1): epilogue, then the switch
     // to the next item before its first QK.
+    // The group in its M phase issues at raised wave priority, so that the
+    // other group's softmax instructions fill the gaps between its matrix
+    // products rather than delay them (d >= 128: 0.5-3 % faster; d = 64, where
+    // a phase has half the products, 2 % slower).
     auto phase_m = [&](int g, int step) {
+        if constexpr (D >= 128) __builtin_amdgcn_s_setprio(1);
         if constexpr (STREAM) {
             pv(g);
             if (g == cur_start + cur.T) {
@@ -675,6 +680,7 @@ void fwd_pp_kernel(FwdParams p) {
             pv(g);
         }
         qk(g);
+        if constexpr (D >= 128) __builtin_amdgcn_s_setprio(0);
     };
     // ---- V phase g: online softmax of S_g -> P_g (bf16), O rescaled if needed.
     auto phase_v = [&](int g) {
