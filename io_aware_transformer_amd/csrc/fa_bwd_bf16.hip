@@ -389,10 +389,10 @@ void bwd_dkdv2_kernel(BwdParams p) {
                 }
             }
         }
-        // This wave's copies of the next tile are done once only the newest
-        // tile's remain; drain this wave's LDS reads (the stage just read is
-        // refilled next) and meet at a plain barrier: a __syncthreads()
-        // fence would also wait for the copy of the newest tile.
+        // This wave's copies of the next tile are done once only those of the
+        // tiles issued after it remain; drain this wave's LDS reads (the stage
+        // just read is refilled next) and meet at a plain barrier: a
+        // __syncthreads() fence would also wait for the newer copies.
         wait_older(min(iters - 1, t + 3) - (t + 1));
         barrier_lds();
     }
@@ -1009,7 +1009,7 @@ void bwd_dq2_kernel(BwdParams p) {
             }
         }
         // as in the dK/dV kernel: own copies of the next tile, LDS reads
-        // drained, plain barrier (no fence waiting for the newest copy)
+        // drained, plain barrier (no fence waiting for the newer copies)
         const int ahead = min(ntiles - 1, kt + 3) - (kt + 1);  // tiles issued after kt + 1
         if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * PPW) & 15) | (((4 * PPW) >> 4) << 14));
         else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PPW) & 15) | (((2 * PPW) >> 4) << 14));
